@@ -1,0 +1,243 @@
+/*
+ * hyattn -- per-layer attention step of a hybrid full/linear-attention model
+ * on AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * Pages cited (by title and section):
+ *   P2 = "推理框架适配Hybrid Model：KV Cache管理与算子调度实战"
+ *   P1 = "Hybrid Model推理适配：vLLM与SGLang的工程实践指南"
+ *
+ * What the library computes (P2 §2.1, §2.3):
+ *   - linear layers keep, per request and head, a D x D fp32 state S. Each new
+ *     token adds k (x) v to S (S[i][j] += k[i] * v[j]) and the layer outputs
+ *     o = q . S (o[j] = sum_i q[i] S[i][j]) using the state that already holds
+ *     that token. Chunked prefill gives the same result chunk by chunk
+ *     (P2 §2.4); decode updates S in place.
+ *   - full layers keep K and V in a pool of 16-token blocks reached through a
+ *     per-request block table; attention is softmax(scale * q . k) . v over
+ *     the request's cached tokens (causal inside a prefill chunk).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory. Host pointers are marked "host".
+ *   - Element types: q/k/v/o and KV pools are fp32 or bf16 (hyattn_dtype);
+ *     linear states are always fp32. bf16 outputs are rounded to nearest-even.
+ *   - Layouts are row-major, innermost dimension last:
+ *       packed tokens  [N_tok][H][D]         (token-major)
+ *       KV pool        [n_blocks][H_kv][16][D]
+ *       block tables   int32 [B][max_blocks_per_seq], -1 = unused entry
+ *       state pool     fp32 [n_linear_layers][n_slots][H][D][D]
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call that
+ *     launches work is asynchronous on that stream and never synchronizes,
+ *     except in checked mode (environment HYATTN_CHECK=1), where calls copy
+ *     index arrays to the host and validate their contents first.
+ *   - Errors: every call validates its arguments before launching anything;
+ *     a call that fails has no side effects. The message of the last failure
+ *     on the calling thread is returned by hyattn_last_error().
+ *   - Supported head dims: D = 64 and D = 128.
+ */
+#ifndef HYATTN_H
+#define HYATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HYATTN_OK = 0,
+  HYATTN_ERR_INVALID_ARG = 1,       /* null pointer, bad size, bad index content */
+  HYATTN_ERR_OUT_OF_SLOTS = 2,      /* state pool exhausted (P2 §4.2, second OOM kind) */
+  HYATTN_ERR_BAD_SLOT = 3,          /* slot id out of range, not allocated, or never zeroed */
+  HYATTN_ERR_UNSUPPORTED_LAYER = 4, /* a layer type outside hyattn_layer_type (P1 §4.3) */
+  HYATTN_ERR_UNSUPPORTED = 5,       /* D, dtype or chunk size without a kernel */
+  HYATTN_ERR_HIP = 6                /* a HIP runtime call or launch failed */
+} hyattn_status;
+
+typedef enum { HYATTN_F32 = 0, HYATTN_BF16 = 1 } hyattn_dtype;
+
+/* Layer types of the model config (P2 §2.2 "layer_types"). */
+typedef enum { HYATTN_LAYER_LINEAR = 0, HYATTN_LAYER_FULL = 1 } hyattn_layer_type;
+
+typedef struct hyattn_state_pool hyattn_state_pool; /* opaque host-side handle */
+
+/* Thread-local text of the last error ("" after success). Never NULL. */
+const char* hyattn_last_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int hyattn_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * State pool (P2 §1.3, §2.2, §2.3): a fixed-size fp32 state per request and
+ * linear layer, separate from the paged KV pool, allocated and zeroed when a
+ * request starts and released when it ends. Its size does not depend on the
+ * sequence length.
+ */
+
+/* Bytes of a pool: n_linear_layers * n_slots * H * D * D * 4. 0 on overflow. */
+size_t hyattn_state_pool_bytes(int n_linear_layers, int n_slots, int H, int D);
+
+/* Wrap a caller-owned device buffer of at least hyattn_state_pool_bytes()
+ * bytes (16-byte aligned). The handle owns only host bookkeeping; all slots
+ * start free. */
+hyattn_status hyattn_state_pool_create(void* dev_buf, size_t bytes, int n_linear_layers,
+                                       int n_slots, int H, int D, hyattn_state_pool** out);
+
+/* Release the handle (not the device buffer). NULL is accepted. */
+hyattn_status hyattn_state_pool_destroy(hyattn_state_pool* pool);
+
+/* Host, synchronous, thread-safe. Reserve n slots: the n lowest free ids in
+ * ascending order are written to slots_out (host). All-or-nothing: fails with
+ * HYATTN_ERR_OUT_OF_SLOTS and changes nothing when fewer than n are free. */
+hyattn_status hyattn_state_pool_alloc(hyattn_state_pool* pool, int n, int32_t* slots_out);
+
+/* Zero the state of the given slots in every linear layer (request start).
+ * slots_dev: device int32[n]; asynchronous on `stream`. In checked mode the
+ * slots must be allocated. Marks the slots as zeroed for checked mode. */
+hyattn_status hyattn_state_pool_zero(hyattn_state_pool* pool, const int32_t* slots_dev, int n,
+                                     void* stream);
+
+/* Host, synchronous. Return slots (host int32[n]) to the pool. Fails with
+ * HYATTN_ERR_BAD_SLOT, changing nothing, if an id is out of range, not
+ * allocated, or repeated. */
+hyattn_status hyattn_state_pool_free(hyattn_state_pool* pool, const int32_t* slots, int n);
+
+/* Number of slots currently allocated (the pool's memory-usage verb), or -1. */
+int hyattn_state_pool_in_use(const hyattn_state_pool* pool);
+
+/* Device address of the state S[layer][slot][0][0][0], or NULL if out of range. */
+void* hyattn_state_pool_state_ptr(const hyattn_state_pool* pool, int linear_layer, int slot);
+
+/* ---------------------------------------------------------------------------
+ * Linear layers (P2 §2.1 recurrence; P2 §2.3 contract (Q, K, V, previous
+ * state) -> (output, new state); P2 §2.4 chunked prefill).
+ */
+
+/* Chunked prefill of n_req packed requests on linear layer `linear_layer`.
+ *   q, k, v, o   [N_tok][H][D], dtype; request r owns tokens
+ *                cu_seqlens[r] .. cu_seqlens[r+1]-1 (device int32[n_req+1],
+ *                non-decreasing, cu_seqlens[0] = 0).
+ *   slots_dev    device int32[n_req]: the state slot of each request; the
+ *                state is read as the prior state and overwritten in place.
+ *   chunk_size   tokens per chunk: a multiple of 16 in [16, 256] (bf16);
+ *                in [1, 128] for fp32 I/O. For each chunk c (the last may be
+ *                shorter): O_c = Q_c S + tril(Q_c K_c^T) V_c, then
+ *                S <- S + K_c^T V_c.
+ * Requests with zero tokens are left untouched. */
+hyattn_status hyattn_linear_prefill_chunked(hyattn_state_pool* pool, int linear_layer,
+                                            const void* q, const void* k, const void* v, void* o,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* slots_dev, int n_req, int chunk_size,
+                                            hyattn_dtype dtype, void* stream);
+
+/* One decode step for B requests: per request r and head h,
+ * S <- S + k (x) v, then o = q . S.  q, k, v, o: [B][H][D], dtype. */
+hyattn_status hyattn_linear_decode(hyattn_state_pool* pool, int linear_layer, const void* q,
+                                   const void* k, const void* v, void* o,
+                                   const int32_t* slots_dev, int B, hyattn_dtype dtype,
+                                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Full layers: paged KV cache of 16-token blocks (P2 §2.1 page table, P2 §2.3
+ * PagedAttention decode, P1 §2.1 16 tokens per page).
+ *
+ * Logical token p of request r is stored in physical block
+ * block_tables[r][p / 16] at offset p % 16, i.e. element
+ * ((block * H_kv + g) * 16 + p % 16) * D of a pool, for KV head g.
+ * context_lens (device int32[B]) count every cached token INCLUDING the new
+ * ones of this step. Query head h reads KV head h / (H_q / H_kv).
+ */
+
+/* Write new tokens into the pools. k_new, v_new: [N_new][H_kv][D]; request r
+ * owns rows cu_q_lens[r] .. cu_q_lens[r+1]-1 (device int32[B+1]); its i-th
+ * new token goes to logical position context_lens[r] - q_len_r + i.
+ * max_q_len (host) bounds the q lengths. */
+hyattn_status hyattn_paged_append(const void* k_new, const void* v_new, void* k_pool,
+                                  void* v_pool, int64_t n_blocks, const int32_t* block_tables_dev,
+                                  int max_blocks_per_seq, const int32_t* context_lens_dev,
+                                  const int32_t* cu_q_lens_dev, int B, int max_q_len, int H_kv,
+                                  int D, hyattn_dtype dtype, void* stream);
+
+/* Workspace (device bytes) needed by hyattn_paged_decode for B requests whose
+ * contexts are at most max_context tokens. */
+size_t hyattn_paged_decode_workspace_bytes(int B, int H_q, int D, int max_context);
+
+/* Decode attention: one query per request (the token at position
+ * context_lens[r] - 1, already appended). q, o: [B][H_q][D], dtype.
+ * o = softmax(scale * q K_r^T) V_r over the context_lens[r] cached tokens;
+ * context_lens[r] == 0 gives o = 0. max_context (host) bounds context_lens.
+ * workspace: device buffer of hyattn_paged_decode_workspace_bytes() bytes. */
+hyattn_status hyattn_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                  int64_t n_blocks, const int32_t* block_tables_dev,
+                                  int max_blocks_per_seq, const int32_t* context_lens_dev,
+                                  int max_context, int B, int H_q, int H_kv, int D, float scale,
+                                  void* workspace, size_t workspace_bytes, hyattn_dtype dtype,
+                                  void* stream);
+
+/* Causal prefill attention over paged KV (FlashAttention-style, P2 §2.3): the
+ * i-th query of request r (row cu_q_lens[r] + i of q/o, [N_q][H_q][D]) sits at
+ * position context_lens[r] - q_len_r + i and attends to keys 0 .. that
+ * position, all read through the block table (earlier chunks included). */
+hyattn_status hyattn_paged_prefill(const void* q, void* o, const void* k_pool,
+                                   const void* v_pool, int64_t n_blocks,
+                                   const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                   const int32_t* context_lens_dev, const int32_t* cu_q_lens_dev,
+                                   int max_q_len, int B, int H_q, int H_kv, int D, float scale,
+                                   hyattn_dtype dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * One attention step over all layers of a hybrid model (P2 §2.2 layer-type
+ * registration and per-forward metadata; P1 §3.2 per-layer dispatch plan).
+ */
+typedef struct {
+  const void* q; /* linear: [N][H][D];  full: [N][H][D]            */
+  const void* k; /* linear: [N][H][D];  full: new keys [N][H_kv][D]   */
+  const void* v; /* linear: [N][H][D];  full: new values [N][H_kv][D] */
+  void* o;       /* [N][H][D] */
+  void* k_pool;  /* full layers: [n_blocks][H_kv][16][D]; linear: unused */
+  void* v_pool;
+} hyattn_layer_io;
+
+typedef struct {
+  int n_prefill;                /* requests bringing a prompt chunk (rows first)  */
+  int n_decode;                 /* requests bringing one token (rows after those) */
+  const int32_t* cu_seqlens;    /* device [n_prefill+1], prefill token offsets    */
+  int n_prefill_tokens;         /* host: cu_seqlens[n_prefill] (decode rows start here) */
+  int max_prefill_len;          /* host bound on prefill chunk lengths            */
+  const int32_t* prefill_slots; /* device [n_prefill] state slots                 */
+  const int32_t* decode_slots;  /* device [n_decode] state slots                  */
+  const int32_t* block_tables;  /* device [n_prefill+n_decode][max_blocks_per_seq] */
+  int max_blocks_per_seq;
+  const int32_t* context_lens;  /* device [n_prefill+n_decode], new tokens included */
+  const int32_t* cu_q_lens;     /* device [n_prefill+n_decode+1]: cu_seqlens, then +1 each */
+  int max_context;              /* host bound on context_lens                     */
+  int64_t n_blocks;             /* blocks in each full layer's pool               */
+  int H;                        /* heads of linear layers = query heads of full layers */
+  int H_kv;                     /* KV heads of full layers                        */
+  int D;
+  int chunk_size;               /* linear chunked prefill                         */
+  float scale;                  /* softmax scale of full layers                   */
+  hyattn_dtype dtype;
+  void* workspace;              /* device, hyattn_hybrid_workspace_bytes() bytes  */
+  size_t workspace_bytes;
+} hyattn_batch;
+
+size_t hyattn_hybrid_workspace_bytes(const hyattn_batch* batch);
+
+/* layer_types: host int32[n_layers], each HYATTN_LAYER_LINEAR or _FULL; all
+ * are checked before anything is launched (HYATTN_ERR_UNSUPPORTED_LAYER).
+ * Linear layers are numbered 0, 1, ... in order of appearance and use that
+ * layer of the state pool; each full layer uses its own k_pool/v_pool.
+ * Per linear layer: chunked prefill of the prefill requests, then decode of
+ * the decode requests. Per full layer: append the new K/V of every request,
+ * causal prefill attention for the prefill requests, decode attention for
+ * the decode requests. All launches go to `stream` in layer order. */
+hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
+                                 const hyattn_layer_io* layers, const hyattn_batch* batch,
+                                 hyattn_state_pool* pool, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYATTN_H */

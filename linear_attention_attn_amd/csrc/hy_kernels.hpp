@@ -1,0 +1,50 @@
+// Host-side launchers of the hyattn gfx950 kernels (internal to the library).
+// Each launcher assumes its arguments were validated by the C-ABI layer and
+// returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hy {
+
+// ---- linear layers ------------------------------------------------------------
+hipError_t launch_state_zero(float* pool, int n_layers, int n_slots, int64_t slot_elems,
+                             const int32_t* slots, int n, hipStream_t s);
+
+hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q, const void* k,
+                                const void* v, void* o, const int32_t* slots, int B, int H, int D,
+                                bool bf16, hipStream_t s);
+
+hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q, const void* k,
+                                 const void* v, void* o, const int32_t* cu, const int32_t* slots,
+                                 int n_req, int H, int D, int chunk, bool bf16, hipStream_t s);
+
+// Largest chunk the fp32-I/O prefill kernel takes (its chunk scores live in LDS).
+constexpr int kMaxChunkF32 = 128;
+
+// ---- full layers --------------------------------------------------------------
+hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                               int64_t n_blocks, const int32_t* bt, int max_blocks,
+                               const int32_t* ctx, const int32_t* cu_q, int B, int max_q_len,
+                               int H_kv, int D, bool bf16, hipStream_t s);
+
+struct DecodePlan {
+  int part_blocks;  // 16-token blocks per context partition
+  int max_parts;    // partitions of the longest context
+};
+DecodePlan decode_plan(int max_context);
+size_t decode_workspace_bytes(int B, int H_q, int D, int max_context);
+
+hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
+                               int64_t n_blocks, const int32_t* bt, int max_blocks,
+                               const int32_t* ctx, int max_context,
+                               int B, int H_q, int H_kv, int D, float scale, void* workspace,
+                               bool bf16, hipStream_t s);
+
+hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                const int32_t* ctx,
+                                const int32_t* cu_q, int max_q_len, int B, int H_q, int H_kv,
+                                int D, float scale, bool bf16, hipStream_t s);
+
+}  // namespace hy

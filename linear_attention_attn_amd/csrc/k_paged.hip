@@ -1,0 +1,458 @@
+// Full-attention kernels over a paged KV cache of 16-token blocks for gfx950:
+// KV append, split-context decode with a log-sum-exp merge, and causal
+// prefill.
+//
+// Method (page "推理框架适配Hybrid Model：KV Cache管理与算子调度实战", "P2"):
+//   §2.1  KV is cut into fixed 16-token blocks mapped through a per-request
+//         page (block) table; full-attention decode costs O(S * D) per token.
+//   §2.3  decode is PagedAttention over Q, K, V and the block table; prefill a
+//         FlashAttention-class kernel.
+// Layout: pool [n_blocks][H_kv][16][D]; logical token p of request r lives in
+// block bt[r][p / 16] at offset p % 16; query head h reads KV head
+// h / (H_q / H_kv). Softmax is evaluated in base 2 on scores pre-multiplied by
+// scale * log2(e), with the running maximum subtracted (fp32 throughout).
+#include <math.h>
+
+#include "hy_common.hpp"
+#include "hy_kernels.hpp"
+
+namespace hy {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ============================================================================
+// Append: copy each new token's K and V rows into its slot. grid (token tiles
+// of 16, B); 16-byte vector copies.
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void k_paged_append(const T* __restrict__ k_new,
+                                                      const T* __restrict__ v_new,
+                                                      T* __restrict__ k_pool, T* __restrict__ v_pool,
+                                                      int64_t n_blocks, const int32_t* __restrict__ bt,
+                                                      int max_blocks, const int32_t* __restrict__ ctx,
+                                                      const int32_t* __restrict__ cu, int H_kv, int D) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int r = blockIdx.y;
+  const int q0 = cu[r], ql = cu[r + 1] - q0;
+  const int c = ctx[r];
+  const int vec_per_tok = H_kv * D / VEC;
+  const int tok_begin = blockIdx.x * 16;
+  for (int idx = threadIdx.x; idx < 16 * vec_per_tok; idx += 256) {
+    const int i = tok_begin + idx / vec_per_tok;
+    if (i >= ql) break;
+    const int e = (idx % vec_per_tok) * VEC;  // element within [H_kv][D]
+    const int g = e / D, d = e - (e / D) * D;
+    const int p = c - ql + i;
+    if (p < 0 || (p >> 4) >= max_blocks) continue;
+    const int32_t blk = bt[(int64_t)r * max_blocks + (p >> 4)];
+    if (blk < 0 || blk >= n_blocks) continue;
+    const int64_t dst = (((int64_t)blk * H_kv + g) * kBlock + (p & 15)) * D + d;
+    const int64_t src = ((int64_t)(q0 + i) * H_kv + g) * D + d;
+    *reinterpret_cast<u32x4*>(k_pool + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+    *reinterpret_cast<u32x4*>(v_pool + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+  }
+}
+
+hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                               int64_t n_blocks, const int32_t* bt, int max_blocks,
+                               const int32_t* ctx, const int32_t* cu_q, int B, int max_q_len,
+                               int H_kv, int D, bool bf16, hipStream_t s) {
+  if (B <= 0 || max_q_len <= 0) return hipSuccess;
+  dim3 grid((unsigned)((max_q_len + 15) / 16), (unsigned)B), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_paged_append<uint16_t>, grid, block, 0, s, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, (uint16_t*)k_pool, (uint16_t*)v_pool, n_blocks, bt,
+                       max_blocks, ctx, cu_q, H_kv, D);
+  else
+    hipLaunchKernelGGL(k_paged_append<float>, grid, block, 0, s, (const float*)k_new,
+                       (const float*)v_new, (float*)k_pool, (float*)v_pool, n_blocks, bt,
+                       max_blocks, ctx, cu_q, H_kv, D);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Decode planning: a request's context is split into partitions of
+// part_blocks blocks; each (request, KV head, partition) is one workgroup and
+// the partial results are merged by log-sum-exp.
+// ============================================================================
+constexpr int kMinPartBlocks = 32;  // 512 tokens
+constexpr int kMaxParts = 64;
+
+DecodePlan decode_plan(int max_context) {
+  const int nblk = (max_context + kBlock - 1) / kBlock;
+  int pb = (nblk + kMaxParts - 1) / kMaxParts;
+  if (pb < kMinPartBlocks) pb = kMinPartBlocks;
+  int parts = (nblk + pb - 1) / pb;
+  if (parts < 1) parts = 1;
+  return DecodePlan{pb, parts};
+}
+
+size_t decode_workspace_bytes(int B, int H_q, int D, int max_context) {
+  const DecodePlan p = decode_plan(max_context);
+  return (size_t)B * H_q * p.max_parts * (size_t)(D + 2) * sizeof(float);
+}
+
+// ============================================================================
+// Decode, bf16 (MFMA scores). grid (max_parts, H_kv, B), 4 waves.
+//
+// Each wave takes every 4th block of the partition. Scores of the G query
+// heads sharing KV head g against the block's 16 keys come from four
+// v_mfma_f32_16x16x32_bf16 (A = the 16 K rows, B = the query heads padded to
+// 16 columns); lane l then holds keys 4*(l/16)+i of head l%16. For P.V the
+// lane owns value dims DPL*(l%16) .. +DPL of keys 4*(l/16)+i, so the weights
+// it needs sit in its own 16-lane row and are fetched with shuffles.
+// ============================================================================
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_paged_decode_bf16(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ ctx, int H_q, int H_kv, float scale_log2,
+    int part_blocks, int max_parts, float* __restrict__ ws) {
+  constexpr int KS = D / 32;    // k steps of the score MFMA
+  constexpr int DPL = D / 16;   // value dims per lane in P.V
+  constexpr int NW = 4;
+  const int part = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int c = min(ctx[r], max_blocks * kBlock);  // defensive: never read past the table
+  const int nblk = (c + kBlock - 1) / kBlock;
+  const int n_parts = min((nblk + part_blocks - 1) / part_blocks, max_parts);
+  if (part >= n_parts) return;
+  const int b_begin = part * part_blocks;
+  const int b_end = min(nblk, b_begin + part_blocks);
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int h0 = g * G;
+
+  // query fragment (B operand): column lr = head h0 + lr (zero beyond G)
+  u32x4 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (lr < G)
+      qf[s] = *reinterpret_cast<const u32x4*>(q + ((int64_t)r * H_q + h0 + lr) * D + 32 * s + 8 * lg);
+    else
+      qf[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  float m_all[G], l_part[G], acc[G][DPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m_all[hh] = -INFINITY;
+    l_part[hh] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
+  }
+  float m_own = -INFINITY;  // running max of head lr (lanes lr < G)
+
+  const int32_t* btr = bt + (int64_t)r * max_blocks;
+  const int64_t head_stride = (int64_t)kBlock * D;
+
+  for (int b = b_begin + w; b < b_end; b += NW) {
+    const int32_t blk = btr[b];
+    if (blk < 0 || blk >= n_blocks) continue;  // defensive: invalid ids are skipped
+    const int64_t base = ((int64_t)blk * H_kv + g) * head_stride;
+    const uint16_t* kblk = k_pool + base;
+    const uint16_t* vblk = v_pool + base;
+    u32x4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kf[s] = *reinterpret_cast<const u32x4*>(kblk + lr * D + 32 * s + 8 * lg);
+    // value rows 4*lg + i, dims DPL*lr .. +DPL
+    uint32_t vr[4][DPL / 2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* vp = vblk + (4 * lg + i) * D + DPL * lr;
+      if constexpr (DPL == 8) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vp);
+        vr[i][0] = x[0]; vr[i][1] = x[1]; vr[i][2] = x[2]; vr[i][3] = x[3];
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+        vr[i][0] = x[0]; vr[i][1] = x[1];
+      }
+    }
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) sc = mfma16x16x32(kf[s], qf[s], sc);
+
+    // scores: key 16b + 4*lg + i of head lr
+    float x[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = 16 * b + 4 * lg + i < c;
+      x[i] = valid ? sc[i] * scale_log2 : -INFINITY;
+      bm = fmaxf(bm, x[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_own_new = fmaxf(m_own, bm);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_own_new);
+    m_own = m_own_new;
+
+    float corr[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float bmh = __shfl(bm, hh);
+      const float mn = fmaxf(m_all[hh], bmh);
+      corr[hh] = fast_exp2(m_all[hh] - mn);
+      m_all[hh] = mn;
+    }
+    // values of keys beyond the context are masked (the pool may hold junk there)
+    bool vvalid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vvalid[i] = 16 * b + 4 * lg + i < c;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float ph[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ph[i] = __shfl(p[i], 16 * lg + hh);
+      float ls = l_part[hh] * corr[hh];
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr[hh];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!vvalid[i]) continue;
+        ls += ph[i];
+#pragma unroll
+        for (int d2 = 0; d2 < DPL / 2; ++d2) {
+          acc[hh][2 * d2] = __builtin_fmaf(ph[i], bf16_lo(vr[i][d2]), acc[hh][2 * d2]);
+          acc[hh][2 * d2 + 1] = __builtin_fmaf(ph[i], bf16_hi(vr[i][d2]), acc[hh][2 * d2 + 1]);
+        }
+      }
+      l_part[hh] = ls;
+    }
+  }
+
+  // ---- combine the 4 token rows of the wave (same running max) ----
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    l_part[hh] += __shfl_xor(l_part[hh], 16);
+    l_part[hh] += __shfl_xor(l_part[hh], 32);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) {
+      acc[hh][d] += __shfl_xor(acc[hh][d], 16);
+      acc[hh][d] += __shfl_xor(acc[hh][d], 32);
+    }
+  }
+  // ---- combine the 4 waves ----
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ float s_acc[NW][G][D];
+  if (l < 16) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) s_acc[w][hh][DPL * lr + d] = acc[hh][d];
+  }
+  if (l == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      s_m[w][hh] = m_all[hh];
+      s_l[w][hh] = l_part[hh];
+    }
+  }
+  __syncthreads();
+  const bool single = (n_parts == 1);
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int hh = idx / D, d = idx - (idx / D) * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][hh]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = (s_m[ww][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][hh] - M);
+      L += s_l[ww][hh] * f;
+      A += s_acc[ww][hh][d] * f;
+    }
+    const int head = h0 + hh;
+    if (single) {
+      o[((int64_t)r * H_q + head) * D + d] = (uint16_t)f32_to_bf16_bits(A / L);
+    } else {
+      float* wp = ws + (((int64_t)r * H_q + head) * max_parts + part) * (D + 2);
+      wp[2 + d] = A;
+      if (d == 0) {
+        wp[0] = M;
+        wp[1] = L;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Merge of the partition partials: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// grid B * H_q, D threads. Requests with one partition were written directly;
+// an empty context gives zeros.
+// ============================================================================
+template <typename T>
+__global__ void k_paged_merge(T* __restrict__ o, const int32_t* __restrict__ ctx, int max_blocks,
+                              int H_q, int D, int part_blocks, int max_parts,
+                              const float* __restrict__ ws) {
+  const int rh = blockIdx.x;
+  const int r = rh / H_q;
+  const int c = min(ctx[r], max_blocks * kBlock);
+  const int nblk = (c + kBlock - 1) / kBlock;
+  const int n_parts = min((nblk + part_blocks - 1) / part_blocks, max_parts);
+  if (n_parts == 1) return;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float out = 0.f;
+    if (n_parts > 1) {
+      const float* wp = ws + (int64_t)rh * max_parts * (D + 2);
+      float M = -INFINITY;
+      for (int p = 0; p < n_parts; ++p) M = fmaxf(M, wp[p * (D + 2)]);
+      float L = 0.f, A = 0.f;
+      for (int p = 0; p < n_parts; ++p) {
+        const float f = fast_exp2(wp[p * (D + 2)] - M);
+        L += wp[p * (D + 2) + 1] * f;
+        A += wp[p * (D + 2) + 2 + d] * f;
+      }
+      out = A / L;
+    }
+    io<T>::st(o, (int64_t)rh * D + d, out);
+  }
+}
+
+// ============================================================================
+// Simple paged attention (VALU), any dtype, decode or causal prefill: one wave
+// per (query row, head). Each lane runs an online softmax over keys
+// lane, lane+64, ...; lanes are merged by log-sum-exp through LDS. Used for
+// fp32 I/O.
+// ============================================================================
+template <int D, typename T>
+__global__ __launch_bounds__(64) void k_paged_attn_simple(
+    const T* __restrict__ q, T* __restrict__ o, const T* __restrict__ k_pool,
+    const T* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
+    int H_kv, float scale_log2) {
+  const int i = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
+  const int q0 = cu_q ? cu_q[r] : r;
+  const int ql = cu_q ? cu_q[r + 1] - q0 : 1;
+  if (i >= ql) return;
+  const int row = q0 + i;
+  const int n_keys = min(ctx[r] - ql + i + 1, max_blocks * kBlock);
+  const int g = h / (H_q / H_kv);
+  const int lane = threadIdx.x;
+  __shared__ float sq[D];
+  __shared__ float sacc[64][D + 1];
+  __shared__ float sm[64], sl[64];
+  for (int d = lane; d < D; d += 64) sq[d] = io<T>::ld(q, ((int64_t)row * H_q + h) * D + d);
+  __syncthreads();
+  float m = -INFINITY, lsum = 0.f;
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  const int32_t* btr = bt + (int64_t)r * max_blocks;
+  for (int p = lane; p < n_keys; p += 64) {
+    const int32_t blk = btr[p >> 4];
+    if (blk < 0 || blk >= n_blocks) continue;  // defensive: invalid ids are skipped
+    const int64_t base = (((int64_t)blk * H_kv + g) * kBlock + (p & 15)) * D;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = __builtin_fmaf(sq[d], io<T>::ld(k_pool, base + d), s);
+    s *= scale_log2;
+    const float mn = fmaxf(m, s);
+    const float corr = fast_exp2(m - mn);
+    const float pw = fast_exp2(s - mn);
+    lsum = lsum * corr + pw;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(pw, io<T>::ld(v_pool, base + d), acc[d] * corr);
+    m = mn;
+  }
+  sm[lane] = m;
+  sl[lane] = lsum;
+#pragma unroll
+  for (int d = 0; d < D; ++d) sacc[lane][d] = acc[d];
+  __syncthreads();
+  float M = -INFINITY;
+  for (int j = 0; j < 64; ++j) M = fmaxf(M, sm[j]);
+  for (int d = lane; d < D; d += 64) {
+    float L = 0.f, A = 0.f;
+    if (n_keys > 0) {
+      for (int j = 0; j < 64; ++j) {
+        const float f = (sm[j] == -INFINITY) ? 0.f : fast_exp2(sm[j] - M);
+        L += sl[j] * f;
+        A += sacc[j][d] * f;
+      }
+    }
+    io<T>::st(o, ((int64_t)row * H_q + h) * D + d, n_keys > 0 ? A / L : 0.f);
+  }
+}
+
+template <int D, typename T>
+static hipError_t launch_simple(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                const int32_t* ctx, const int32_t* cu_q, int max_q_len, int B,
+                                int H_q, int H_kv, float scale_log2, hipStream_t s) {
+  dim3 grid((unsigned)max_q_len, (unsigned)H_q, (unsigned)B);
+  hipLaunchKernelGGL((k_paged_attn_simple<D, T>), grid, dim3(64), 0, s, (const T*)q, (T*)o,
+                     (const T*)k_pool, (const T*)v_pool, n_blocks, bt, max_blocks, ctx, cu_q, H_q,
+                     H_kv, scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
+                               int64_t n_blocks, const int32_t* bt, int max_blocks,
+                               const int32_t* ctx, int max_context,
+                               int B, int H_q, int H_kv, int D, float scale, void* workspace,
+                               bool bf16, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const float sl2 = scale * kLog2e;
+  if (!bf16) {
+    if (D == 128)
+      return launch_simple<128, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, nullptr, 1, B,
+                                       H_q, H_kv, sl2, s);
+    return launch_simple<64, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, nullptr, 1, B, H_q,
+                                    H_kv, sl2, s);
+  }
+  const DecodePlan plan = decode_plan(max_context);
+  const int G = H_q / H_kv;
+  float* ws = (float*)workspace;
+  dim3 grid((unsigned)plan.max_parts, (unsigned)H_kv, (unsigned)B), block(256);
+#define HY_PD(DD, GG)                                                                         \
+  hipLaunchKernelGGL((k_paged_decode_bf16<DD, GG>), grid, block, 0, s, (const uint16_t*)q,    \
+                     (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
+                     bt, max_blocks, ctx, H_q, H_kv, sl2, plan.part_blocks, plan.max_parts, ws)
+#define HY_PD_G(DD)                   \
+  switch (G) {                        \
+    case 1: HY_PD(DD, 1); break;      \
+    case 2: HY_PD(DD, 2); break;      \
+    case 4: HY_PD(DD, 4); break;      \
+    case 8: HY_PD(DD, 8); break;      \
+    default: return hipErrorInvalidValue; \
+  }
+  if (D == 128) {
+    HY_PD_G(128)
+  } else {
+    HY_PD_G(64)
+  }
+#undef HY_PD_G
+#undef HY_PD
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // partials of multi-partition requests are merged; empty contexts get zeros
+  hipLaunchKernelGGL(k_paged_merge<uint16_t>, dim3((unsigned)(B * H_q)), dim3(D), 0, s,
+                     (uint16_t*)o, ctx, max_blocks, H_q, D, plan.part_blocks, plan.max_parts, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                const int32_t* ctx,
+                                const int32_t* cu_q, int max_q_len, int B, int H_q, int H_kv,
+                                int D, float scale, bool bf16, hipStream_t s) {
+  if (B <= 0 || max_q_len <= 0) return hipSuccess;
+  const float sl2 = scale * kLog2e;
+  if (bf16) {
+    if (D == 128)
+      return launch_simple<128, uint16_t>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q,
+                                          max_q_len, B, H_q, H_kv, sl2, s);
+    return launch_simple<64, uint16_t>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q, max_q_len,
+                                       B, H_q, H_kv, sl2, s);
+  }
+  if (D == 128)
+    return launch_simple<128, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q, max_q_len,
+                                     B, H_q, H_kv, sl2, s);
+  return launch_simple<64, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q, max_q_len, B,
+                                  H_q, H_kv, sl2, s);
+}
+
+}  // namespace hy

@@ -1,0 +1,88 @@
+"""Helpers shared by the GPU parity tests: host<->device copies of stored
+tensors and the tolerance rules.
+
+Tolerances (the fp32 and bf16 rules applied to every parity comparison):
+  * fp32 I/O: max_i |g_i - r_i| / max(|r_i|, RMS(r)) <= 1e-4.
+  * bf16 I/O: max_i |g_i - r_i| / RMS(r) <= 2e-2 and mean_i |g_i - r_i| / RMS(r)
+    <= 5e-3, RMS over the whole compared tensor.
+  * fp32 states in bf16 runs use the fp32 rule.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TOL_F32 = 1e-4
+TOL_BF16_MAX = 2e-2
+TOL_BF16_MEAN = 5e-3
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev(a: np.ndarray):
+    """Upload a stored tensor: uint16 arrays become bfloat16, others keep dtype."""
+    t = torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return t.from_numpy(a.view(np.int16)).view(t.bfloat16).cuda()
+    return t.from_numpy(a).cuda()
+
+
+def host(x) -> np.ndarray:
+    """Download: bfloat16 tensors come back as uint16 bit patterns."""
+    t = torch()
+    x = x.detach()
+    if x.dtype == t.bfloat16:
+        return x.view(t.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def err_f32(g, r):
+    g, r = as_f64(np.asarray(g)), np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    den = np.maximum(np.abs(r), rms if rms > 0 else 1e-300)
+    return float(np.max(np.abs(g - r) / den)) if r.size else 0.0
+
+
+def err_bf16(g, r):
+    g, r = as_f64(np.asarray(g)), np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r)))
+    d = np.abs(g - r) / (rms if rms > 0 else 1.0)
+    return float(d.max()), float(d.mean())
+
+
+def assert_f32(g, r, what="", tol=TOL_F32):
+    e = err_f32(g, r)
+    assert np.isfinite(as_f64(np.asarray(g))).all(), f"{what}: non-finite values"
+    assert e <= tol, f"{what}: fp32 max rel error {e:.3e} > {tol:.0e}"
+    return e
+
+
+def assert_bf16(g, r, what=""):
+    assert np.isfinite(as_f64(np.asarray(g))).all(), f"{what}: non-finite values"
+    mx, mean = err_bf16(g, r)
+    assert mx <= TOL_BF16_MAX and mean <= TOL_BF16_MEAN, (
+        f"{what}: bf16 errors max {mx:.3e} (<= {TOL_BF16_MAX}), mean {mean:.3e} (<= {TOL_BF16_MEAN})")
+    return mx, mean
+
+
+def assert_io(g, r, dtype: str, what=""):
+    return assert_f32(g, r, what) if dtype == "f32" else assert_bf16(g, r, what)
+
+
+def torch_dtype(dtype: str):
+    t = torch()
+    return t.bfloat16 if dtype == "bf16" else t.float32
+
+
+def i32(a):
+    t = torch()
+    return t.as_tensor(np.asarray(a, dtype=np.int32)).cuda()

@@ -1,0 +1,91 @@
+"""Run a synth.hybrid case through hyattn_hybrid_step and through the oracle.
+
+Shared by the GPU hybrid tests and the smoke check. The HIP side sees only
+device copies of the case's arrays; the oracle side sees only the host arrays.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import ref
+from tests import gpu_util as gu
+
+
+def run_gpu(case, slot_perm=None):
+    import torch
+    from linear_attention_attn_amd import hyattn as hy
+    from linear_attention_attn_amd import layer_types
+    types = layer_types.parse(case["types"])
+    H, Hkv, D = case["H"], case["Hkv"], case["D"]
+    n_p, n_d = case["n_prefill"], case["n_decode"]
+    B = n_p + n_d
+    n_lin = sum(t == 0 for t in types)
+    lay = case["layout"]
+    n_slots = B + 3
+    nbytes = hy.hyattn_state_pool_bytes(max(n_lin, 1), n_slots, H, D)
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    view = buf.view(max(n_lin, 1), n_slots, H, D, D)
+    pool = hy.hyattn_state_pool_create(buf, nbytes, max(n_lin, 1), n_slots, H, D)
+    slots = hy.hyattn_state_pool_alloc(pool, n_slots)[:B]
+    if slot_perm is not None:
+        slots = [slots[i] for i in slot_perm]
+    hy.hyattn_state_pool_zero(pool, gu.i32(slots), B)  # request start
+    for li in range(n_lin):
+        for r in range(B):
+            view[li, slots[r]] = torch.from_numpy(case["states"][li, r]).cuda()
+    dev_layers, keep = [], []
+    fi = 0
+    for t, io in zip(types, case["layers"]):
+        d = {n: gu.dev(io[n]) for n in ("q", "k", "v")}
+        d["o"] = torch.full_like(d["q"], float("nan"))
+        if t == 1:
+            d["k_pool"], d["v_pool"] = (gu.dev(x) for x in case["pools"][fi])
+            fi += 1
+        dev_layers.append(d)
+    ws_bytes = hy.hyattn_paged_decode_workspace_bytes(n_d, H, D, int(case["ctx"].max()))
+    ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
+    tensors = dict(cu_seqlens=gu.i32(case["prefill_cu"]), prefill_slots=gu.i32(slots[:n_p]),
+                   decode_slots=gu.i32(slots[n_p:]), block_tables=gu.i32(lay.block_tables),
+                   context_lens=gu.i32(case["ctx"]), cu_q_lens=gu.i32(case["cu_q"]), workspace=ws)
+    batch = hy.make_batch(n_prefill=n_p, n_decode=n_d, n_prefill_tokens=int(case["prefill_cu"][-1]),
+                          max_prefill_len=case["max_prefill_len"],
+                          max_blocks_per_seq=lay.max_blocks, max_context=int(case["ctx"].max()),
+                          n_blocks=lay.n_blocks, H=H, H_kv=Hkv, D=D, chunk_size=case["chunk"],
+                          scale=case["scale"], dtype=hy.BF16 if case["dtype"] == "bf16" else hy.F32,
+                          workspace_bytes=ws_bytes, **tensors)
+    hy.hyattn_hybrid_step(types, len(types), dev_layers, batch, pool)
+    torch.cuda.synchronize()
+    outs = [gu.host(d["o"]) for d in dev_layers]
+    states = np.stack([np.stack([gu.host(view[li, slots[r]]) for r in range(B)])
+                       for li in range(n_lin)]) if n_lin else None
+    pools = [(gu.host(d["k_pool"]), gu.host(d["v_pool"])) for t, d in zip(types, dev_layers)
+             if t == 1]
+    hy.hyattn_state_pool_destroy(pool)
+    return outs, states, pools
+
+
+def run_oracle(case, units_linear=None, units_full=None):
+    types = ref.parse_layer_types(case["types"])
+    states = case["states"].astype(np.float64)
+    pools = [(kp.copy(), vp.copy()) for kp, vp in case["pools"]]
+    batch = dict(prefill_cu=case["prefill_cu"], n_decode=case["n_decode"],
+                 block_tables=case["layout"].block_tables, context_lens=case["ctx"],
+                 chunk=case["chunk"], scale=case["scale"])
+    outs = ref.hybrid_step(types, case["layers"], batch, states, pools,
+                           units_linear=units_linear, units_full=units_full)
+    return outs, states, pools
+
+
+def compare(case, got, want, check_pools=True):
+    g_outs, g_states, g_pools = got
+    w_outs, w_states, w_pools = want
+    report = []
+    for i, (g, w) in enumerate(zip(g_outs, w_outs)):
+        report.append((i, case["types"][i], gu.assert_io(g, w, case["dtype"], f"layer {i} output")))
+    if g_states is not None:
+        gu.assert_f32(g_states, w_states, "linear states")
+    if check_pools:
+        for (gk, gv), (wk, wv) in zip(g_pools, w_pools):
+            assert np.array_equal(gk.view(np.uint8), wk.view(np.uint8)), "K pool after append"
+            assert np.array_equal(gv.view(np.uint8), wv.view(np.uint8)), "V pool after append"
+    return report

@@ -1,0 +1,170 @@
+"""CPU tests of the hyattn C ABI: the library loads, exports every entry point
+the header declares, and its host logic (slot free list, argument validation,
+layer-type rejection) behaves as documented. Nothing here launches a kernel:
+every call below returns before touching the device.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from linear_attention_attn_amd import hyattn as hy
+from oracle import ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # a non-NULL, aligned address; never dereferenced on these paths
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hyattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = hy.load()
+    names = header_functions()
+    assert len(names) >= 18
+    assert set(names) == set(hy.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert hy.hyattn_abi_version() == 1
+
+
+def test_library_is_gfx950_code_object():
+    blob = open(hy.lib_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_state_pool_bytes_is_independent_of_sequence_length():
+    # the formula has no sequence-length argument at all (P2 §2.1 constant-size state)
+    assert hy.hyattn_state_pool_bytes(24, 256, 32, 128) == 24 * 256 * 32 * 128 * 128 * 4
+    assert hy.hyattn_state_pool_bytes(-1, 1, 1, 1) == 0
+
+
+def test_slot_pool_matches_reference_simulation():
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 3, 6, 2, 64)
+    sim = ref.SlotAllocator(6)
+    rng = np.random.default_rng(0)
+    held = []
+    for _ in range(300):
+        if rng.random() < 0.55:
+            n = int(rng.integers(0, 4))
+            want = sim.alloc(n)
+            if want is None:
+                with pytest.raises(hy.HyattnError) as e:
+                    hy.hyattn_state_pool_alloc(h, n)
+                assert e.value.status == hy.ERR_OUT_OF_SLOTS
+            else:
+                got = hy.hyattn_state_pool_alloc(h, n)
+                assert got == want
+                held += got
+        elif held:
+            k = int(rng.integers(1, len(held) + 1))
+            idx = rng.choice(len(held), size=k, replace=False)
+            ids = [held[i] for i in idx]
+            assert sim.free(ids)
+            hy.hyattn_state_pool_free(h, ids)
+            held = [x for x in held if x not in ids]
+        assert hy.hyattn_state_pool_in_use(h) == sim.in_use()
+    hy.hyattn_state_pool_destroy(h)
+
+
+def test_slot_free_errors_change_nothing():
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 1, 4, 1, 64)
+    assert hy.hyattn_state_pool_alloc(h, 2) == [0, 1]
+    for bad in ([2], [0, 0], [7], [-1], [0, 3]):
+        with pytest.raises(hy.HyattnError) as e:
+            hy.hyattn_state_pool_free(h, bad)
+        assert e.value.status == hy.ERR_BAD_SLOT
+        assert hy.hyattn_state_pool_in_use(h) == 2
+    hy.hyattn_state_pool_free(h, [1, 0])
+    assert hy.hyattn_state_pool_in_use(h) == 0
+    hy.hyattn_state_pool_destroy(h)
+
+
+def test_state_ptr_layout():
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 3, 5, 2, 128)
+    slot_bytes = 2 * 128 * 128 * 4
+    assert hy.hyattn_state_pool_state_ptr(h, 0, 0) == FAKE
+    assert hy.hyattn_state_pool_state_ptr(h, 2, 3) == FAKE + (2 * 5 + 3) * slot_bytes
+    assert hy.hyattn_state_pool_state_ptr(h, 3, 0) is None
+    hy.hyattn_state_pool_destroy(h)
+
+
+def test_pool_create_validation():
+    for args, st in (((None, 1 << 30, 1, 1, 1, 64), hy.ERR_INVALID_ARG),
+                     ((FAKE, 100, 1, 1, 1, 64), hy.ERR_INVALID_ARG),
+                     ((FAKE + 4, 1 << 30, 1, 1, 1, 64), hy.ERR_INVALID_ARG),
+                     ((FAKE, 1 << 30, 1, 1, 1, 96), hy.ERR_UNSUPPORTED),
+                     ((FAKE, 1 << 30, 0, 1, 1, 64), hy.ERR_INVALID_ARG)):
+        with pytest.raises(hy.HyattnError) as e:
+            hy.hyattn_state_pool_create(*args)
+        assert e.value.status == st, args
+
+
+def test_argument_validation_before_launch():
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 2, 4, 2, 128)
+    P = FAKE
+    cases = [
+        (lambda: hy.hyattn_linear_decode(h, 2, P, P, P, P, P, 1, hy.BF16, 0), hy.ERR_INVALID_ARG),
+        (lambda: hy.hyattn_linear_decode(h, 0, None, P, P, P, P, 1, hy.BF16, 0), hy.ERR_INVALID_ARG),
+        (lambda: hy.hyattn_linear_decode(h, 0, P, P, P, P, P, 1, 7, 0), hy.ERR_UNSUPPORTED),
+        (lambda: hy.hyattn_linear_prefill_chunked(h, 0, P, P, P, P, P, P, 1, 17, hy.BF16, 0),
+         hy.ERR_UNSUPPORTED),
+        (lambda: hy.hyattn_linear_prefill_chunked(h, 0, P, P, P, P, P, P, 1, 512, hy.BF16, 0),
+         hy.ERR_UNSUPPORTED),
+        (lambda: hy.hyattn_linear_prefill_chunked(h, 0, P, P, P, P, P, P, 1, 256, hy.F32, 0),
+         hy.ERR_UNSUPPORTED),
+        (lambda: hy.hyattn_paged_decode(P, P, P, P, 10, P, 4, P, 64, 1, 6, 4, 128, 1.0, P, 1 << 20,
+                                        hy.BF16, 0), hy.ERR_INVALID_ARG),   # 6 % 4 != 0
+        (lambda: hy.hyattn_paged_decode(P, P, P, P, 10, P, 4, P, 65, 1, 8, 4, 128, 1.0, P, 1 << 20,
+                                        hy.BF16, 0), hy.ERR_INVALID_ARG),   # ctx > 16 * max_blocks
+        (lambda: hy.hyattn_paged_decode(P, P, P, P, 10, P, 4, P, 64, 1, 8, 4, 128, 1.0, P, 16,
+                                        hy.BF16, 0), hy.ERR_INVALID_ARG),   # workspace too small
+        (lambda: hy.hyattn_paged_decode(P, P, P, P, 10, P, 4, P, 64, 1, 32, 2, 128, 1.0, P, 1 << 30,
+                                        hy.BF16, 0), hy.ERR_UNSUPPORTED),   # 16 q heads per KV head
+        (lambda: hy.hyattn_paged_prefill(P, P, P, P, 10, P, 4, P, P, 8, 1, 8, 4, 80, 1.0, hy.BF16, 0),
+         hy.ERR_UNSUPPORTED),                                               # D = 80
+        (lambda: hy.hyattn_paged_append(P, P, P, P, 0, P, 4, P, P, 1, 1, 4, 128, hy.BF16, 0),
+         hy.ERR_INVALID_ARG),                                               # no blocks
+    ]
+    for i, (fn, st) in enumerate(cases):
+        with pytest.raises(hy.HyattnError) as e:
+            fn()
+        assert e.value.status == st, (i, e.value)
+    # zero-sized calls are no-ops that succeed without a device
+    hy.hyattn_linear_decode(h, 0, None, None, None, None, None, 0, hy.BF16, 0)
+    hy.hyattn_linear_prefill_chunked(h, 0, None, None, None, None, None, None, 0, 64, hy.BF16, 0)
+    hy.hyattn_state_pool_destroy(h)
+
+
+def test_unknown_layer_type_rejected_before_any_launch():
+    """P1 §4.3: an unsupported attention type is refused; nothing is launched."""
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 2, 4, 2, 128)
+    b = hy.make_batch(n_prefill=0, n_decode=1, decode_slots=FAKE, H=2, H_kv=2, D=128,
+                      chunk_size=64, dtype=hy.BF16, block_tables=FAKE, context_lens=FAKE,
+                      cu_q_lens=FAKE, max_blocks_per_seq=4, n_blocks=8, max_context=64,
+                      workspace=FAKE, workspace_bytes=1 << 20, scale=1.0)
+    layers = [dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, k_pool=FAKE, v_pool=FAKE)] * 3
+    for types in ([0, 2, 1], [1, 0, -1], [5, 5, 5]):
+        with pytest.raises(hy.HyattnError) as e:
+            hy.hyattn_hybrid_step(types, 3, layers, b, h, 0)
+        assert e.value.status == hy.ERR_UNSUPPORTED_LAYER
+        assert "layer" in e.value.message
+    # missing KV pool on a full layer is caught before launches too
+    bad = [dict(layers[0]), dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE)]
+    with pytest.raises(hy.HyattnError) as e:
+        hy.hyattn_hybrid_step([0, 1], 2, bad, b, h, 0)
+    assert e.value.status == hy.ERR_INVALID_ARG
+    hy.hyattn_state_pool_destroy(h)
+
+
+def test_layer_type_spellings_map_like_the_oracle():
+    from linear_attention_attn_amd import layer_types
+    assert layer_types.parse(["linear", "full_attn", "linear_attn", "full"]) == [0, 1, 0, 1]
+    assert layer_types.parse(["linear", "full"]) == ref.parse_layer_types(["linear", "full"])
+    with pytest.raises(ValueError):
+        layer_types.parse(["mamba"])
