@@ -1,0 +1,395 @@
+"""Benchmark of one hybrid attention step on one MI355X.
+
+Workload (synthetic, seeded): a 32-layer hybrid model, layer types
+[linear, linear, linear, full] x 8, H = 32 heads, D = 128, bf16 I/O, fp32
+linear states. One step serves 16 requests bringing a 4096-token prompt chunk
+(from an empty context; linear chunk size 128) and 240 decode requests whose
+contexts are log-uniform in [512, 131072] (the largest forced to 131072),
+full layers with 8 KV heads in 16-token blocks. A step = zero the 16 prefill
+slots (request start) + hyattn_hybrid_step over all 32 layers. Throughput =
+tokens served per second (65 536 prefill + 240 decode tokens per step).
+
+Printed: one JSON line (see the keys below), with the roofline of the dominant
+kernel (paged decode, HBM-bound; HIP events around each of its launches) and
+the fp64 oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+W = synth.WORKLOADS["hybrid_step"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- workload --
+class Workload:
+    """Device-resident inputs of the hybrid step (allocated once)."""
+
+    def __init__(self, scale_ctx: float = 1.0):
+        import torch
+        from linear_attention_attn_amd import hyattn as hy
+        from linear_attention_attn_amd import layer_types
+        self.hy = hy
+        rng = np.random.default_rng(W["seed"])
+        self.H, self.Hkv, self.D = W["H"], W["Hkv"], W["D"]
+        H, Hkv, D = self.H, self.Hkv, self.D
+        self.types = layer_types.parse([W["pattern"][i % 4] for i in range(W["n_layers"])])
+        self.n_lin = sum(t == 0 for t in self.types)
+        self.n_full = len(self.types) - self.n_lin
+        n_p, n_d, P = W["n_prefill"], W["n_decode"], W["prefill_len"]
+        self.n_p, self.n_d = n_p, n_d
+        dec_ctx = synth.loguniform_contexts(rng, n_d, W["ctx_lo"], int(W["ctx_hi"] * scale_ctx))
+        self.ctx = np.concatenate([np.full(n_p, P, np.int32), dec_ctx]).astype(np.int32)
+        lay = synth.paged_layout(rng, self.ctx)
+        self.lay = lay
+        self.N = n_p * P + n_d
+        self.tokens = self.N
+        B = n_p + n_d
+        dev = "cuda"
+        t0 = time.time()
+        # state pool [L_lin][B][H][D][D]: decode requests hold a prior state
+        nbytes = hy.hyattn_state_pool_bytes(self.n_lin, B, H, D)
+        self.state_buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        sv = self.state_buf.view(self.n_lin, B, H * D * D)
+        g = torch.Generator(device=dev)
+        g.manual_seed(W["seed"] * 1000 + 1)
+        for l in range(self.n_lin):
+            sv[l].normal_(0.0, 0.1, generator=g)
+        self.pool = hy.hyattn_state_pool_create(self.state_buf, nbytes, self.n_lin, B, H, D)
+        slots = hy.hyattn_state_pool_alloc(self.pool, B)
+        self.slots_p = torch.tensor(slots[:n_p], dtype=torch.int32, device=dev)
+        self.slots_d = torch.tensor(slots[n_p:], dtype=torch.int32, device=dev)
+        # inputs, shared by all layers of one type; outputs one per type
+        s = D ** -0.5
+        self.lin = dict(q=synth.device_normal_bf16((self.N, H, D), s, W["seed"] * 1000 + 2),
+                        k=synth.device_normal_bf16((self.N, H, D), s, W["seed"] * 1000 + 3),
+                        v=synth.device_normal_bf16((self.N, H, D), s, W["seed"] * 1000 + 4))
+        self.lin["o"] = torch.empty_like(self.lin["q"])
+        self.full = dict(q=synth.device_normal_bf16((self.N, H, D), 1.0, W["seed"] * 1000 + 5),
+                         k=synth.device_normal_bf16((self.N, Hkv, D), 1.0, W["seed"] * 1000 + 6),
+                         v=synth.device_normal_bf16((self.N, Hkv, D), 1.0, W["seed"] * 1000 + 7))
+        self.full["o"] = torch.empty_like(self.full["q"])
+        # one K and one V pool per full layer, fully random (prior context of decode requests)
+        self.pools = []
+        for f in range(self.n_full):
+            kp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, W["seed"] * 1000 + 100 + 2 * f)
+            vp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, W["seed"] * 1000 + 101 + 2 * f)
+            self.pools.append((kp, vp))
+        self.bt = torch.as_tensor(lay.block_tables).to(dev)
+        self.ctx_d = torch.as_tensor(self.ctx).to(dev)
+        cu_p = synth.cu_lens([P] * n_p)
+        self.cu_p_host = cu_p
+        self.cu_p = torch.as_tensor(cu_p).to(dev)
+        self.cu_q = torch.as_tensor(np.concatenate([cu_p, cu_p[-1] + np.arange(1, n_d + 1)])
+                                    .astype(np.int32)).to(dev)
+        self.max_context = int(self.ctx.max())
+        self.ws_bytes = hy.hyattn_paged_decode_workspace_bytes(n_d, H, D, self.max_context)
+        self.ws = torch.empty(max(self.ws_bytes, 4) // 4, dtype=torch.float32, device=dev)
+        self.layers = []
+        fi = 0
+        for t in self.types:
+            if t == 0:
+                self.layers.append(dict(self.lin))
+            else:
+                kp, vp = self.pools[fi]
+                fi += 1
+                self.layers.append(dict(self.full, k_pool=kp, v_pool=vp))
+        self.layer_arr = hy.make_layers(self.layers)
+        self.batch = hy.make_batch(
+            n_prefill=n_p, n_decode=n_d, cu_seqlens=self.cu_p, n_prefill_tokens=n_p * P,
+            max_prefill_len=P, prefill_slots=self.slots_p, decode_slots=self.slots_d,
+            block_tables=self.bt, max_blocks_per_seq=lay.max_blocks, context_lens=self.ctx_d,
+            cu_q_lens=self.cu_q, max_context=self.max_context, n_blocks=lay.n_blocks, H=H,
+            H_kv=Hkv, D=D, chunk_size=W["chunk"], scale=D ** -0.5, dtype=hy.BF16,
+            workspace=self.ws, workspace_bytes=self.ws_bytes)
+        torch.cuda.synchronize()
+        kv_bytes = 2 * self.n_full * lay.n_blocks * Hkv * 16 * D * 2
+        log(f"workload ready in {time.time() - t0:.1f}s: KV {kv_bytes / 1e9:.1f} GB, "
+            f"states {nbytes / 1e9:.1f} GB, contexts sum {int(self.ctx.sum())}, "
+            f"max {self.max_context}, blocks/layer {lay.n_blocks}")
+
+    def step(self, stream=None):
+        hy = self.hy
+        hy.hyattn_state_pool_zero(self.pool, self.slots_p, self.n_p, stream)
+        hy.hyattn_hybrid_step(self.types, len(self.types), self.layer_arr, self.batch, self.pool,
+                              stream)
+
+    # ---- algorithmic work per component (per launch) ----
+    def decode_kv_bytes(self):
+        c = self.ctx[self.n_p:].astype(np.int64)
+        kv = int(c.sum()) * self.Hkv * self.D * 2 * 2           # K and V rows read once
+        qo = self.n_d * self.H * self.D * 2 * 2
+        return kv + qo
+
+    def linear_decode_bytes(self):
+        return self.n_d * self.H * (2 * self.D * self.D * 4 + 4 * self.D * 2)
+
+    def linear_prefill_flops(self):
+        C, D, T = W["chunk"], self.D, W["prefill_len"]
+        # per token-head: Q.S (2D^2) + S update (2D^2) + causal intra-chunk (C+1)D (QK^T and PV)
+        per_tok = 4 * D * D + 2 * (C + 1) * D
+        return self.n_p * T * self.H * per_tok
+
+    def linear_prefill_bytes(self):
+        return self.n_p * W["prefill_len"] * self.H * self.D * 2 * 4 + 2 * self.n_p * self.H * self.D * self.D * 4
+
+    def paged_prefill_flops(self):
+        T, D = W["prefill_len"], self.D
+        return self.n_p * self.H * 4 * D * (T * (T + 1) // 2)
+
+
+# ------------------------------------------------------------- components --
+def component_times(wl, reps=3):
+    """Per-call device time of each layer operation, HIP events on torch's stream."""
+    import torch
+    hy = wl.hy
+    st = torch.cuda.current_stream()
+    n_p, n_d, P = wl.n_p, wl.n_d, W["prefill_len"]
+    off = n_p * P
+    lin, full = wl.lin, wl.full
+    kp, vp = wl.pools[0]
+    row = lambda t: t[off:]
+    calls = {
+        "state_zero": lambda: hy.hyattn_state_pool_zero(wl.pool, wl.slots_p, n_p),
+        "linear_prefill": lambda: hy.hyattn_linear_prefill_chunked(
+            wl.pool, 0, lin["q"], lin["k"], lin["v"], lin["o"], wl.cu_p, wl.slots_p, n_p,
+            W["chunk"], hy.BF16),
+        "linear_decode": lambda: hy.hyattn_linear_decode(
+            wl.pool, 0, row(lin["q"]), row(lin["k"]), row(lin["v"]), row(lin["o"]), wl.slots_d,
+            n_d, hy.BF16),
+        "paged_append": lambda: hy.hyattn_paged_append(
+            full["k"], full["v"], kp, vp, wl.lay.n_blocks, wl.bt, wl.lay.max_blocks, wl.ctx_d,
+            wl.cu_q, n_p + n_d, P, wl.Hkv, wl.D, hy.BF16),
+        "paged_prefill": lambda: hy.hyattn_paged_prefill(
+            full["q"], full["o"], kp, vp, wl.lay.n_blocks, wl.bt, wl.lay.max_blocks, wl.ctx_d,
+            wl.cu_p, P, n_p, wl.H, wl.Hkv, wl.D, wl.D ** -0.5, hy.BF16),
+        "paged_decode": lambda: hy.hyattn_paged_decode(
+            row(full["q"]), row(full["o"]), kp, vp, wl.lay.n_blocks, wl.bt[n_p:],
+            wl.lay.max_blocks, wl.ctx_d[n_p:], wl.max_context, n_d, wl.H, wl.Hkv, wl.D,
+            wl.D ** -0.5, wl.ws, wl.ws_bytes, hy.BF16),
+    }
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn()
+            e1.record(st)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        out[name] = float(np.median(ts))
+    return out
+
+
+def dominant_kernel_roofline(wl, steps):
+    """Average paged-decode launch time over all full layers of `steps` steps."""
+    import torch
+    hy = wl.hy
+    st = torch.cuda.current_stream()
+    n_p, n_d, P = wl.n_p, wl.n_d, W["prefill_len"]
+    off = n_p * P
+    full = wl.full
+    ts = []
+    for _ in range(steps):
+        for kp, vp in wl.pools:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            hy.hyattn_paged_decode(full["q"][off:], full["o"][off:], kp, vp, wl.lay.n_blocks,
+                                   wl.bt[n_p:], wl.lay.max_blocks, wl.ctx_d[n_p:], wl.max_context,
+                                   n_d, wl.H, wl.Hkv, wl.D, wl.D ** -0.5, wl.ws, wl.ws_bytes,
+                                   hy.BF16)
+            e1.record(st)
+            ts.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ts]))
+    nbytes = wl.decode_kv_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(kernel="paged_decode (k_paged_decode_bf16 + k_paged_merge)", bound="hbm",
+                achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                algorithmic_bytes_per_launch=nbytes, avg_launch_ms=round(ms, 4))
+
+
+# ------------------------------------------------------------ cpu baseline --
+def cpu_baseline(wl):
+    """Time the fp64 oracle on a bounded sample of the step; extrapolate to tokens/s.
+
+    Each operation type runs a sample of its independent (request, head) units
+    on all host threads at once; its measured rate (work per wall second) is
+    applied to the whole step's work of that type.
+    """
+    import torch
+    from oracle import ref
+    threads = ref.n_threads()
+    rng = np.random.default_rng(123)
+    D, H = wl.D, wl.H
+    P, C = W["prefill_len"], W["chunk"]
+    off = wl.n_p * P
+
+    def host_bf16(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rates = {}
+    # (1) linear chunked prefill: `threads` (request 0, head) units of 4096 tokens
+    nu = min(threads, H)
+    q, k, v = (host_bf16(wl.lin[n][:P]) for n in ("q", "k", "v"))
+    st = np.zeros((1, H, D, D))
+    t0 = time.time()
+    ref.linear_prefill(q, k, v, [0, P], st, chunk=C, units=[(0, h) for h in range(nu)],
+                       threads=threads)
+    rates["linear_prefill_units_per_s"] = nu / (time.time() - t0)
+    # (2) linear decode: 64 requests x all heads
+    nr = 64
+    qd, kd, vd = (host_bf16(wl.lin[n][off:off + nr]) for n in ("q", "k", "v"))
+    std = rng.standard_normal((nr, H, D, D)) * 0.1
+    t0 = time.time()
+    ref.linear_decode(qd, kd, vd, std, threads=threads)
+    rates["linear_decode_units_per_s"] = nr * H / (time.time() - t0)
+    # (3) paged decode: 4 sampled decode requests, all heads, all their keys
+    kp, vp = wl.pools[0]
+    keys = 0
+    t_pd = 0.0
+    for r in rng.choice(np.arange(wl.n_p, wl.n_p + wl.n_d), size=4, replace=False):
+        n = int(wl.ctx[r]); nb = (n + 15) // 16
+        idx = torch.as_tensor(wl.lay.block_tables[r, :nb]).cuda()
+        kk, vv = host_bf16(kp[idx]), host_bf16(vp[idx])
+        qq = host_bf16(wl.full["q"][off + r - wl.n_p: off + r - wl.n_p + 1])
+        t0 = time.time()
+        ref.paged_attention(qq, kk, vv, np.arange(nb, dtype=np.int32)[None], [n], [0, 1],
+                            D ** -0.5, threads=threads)
+        t_pd += time.time() - t0
+        keys += n * H
+    rates["paged_decode_head_keys_per_s"] = keys / t_pd
+    # (4) causal prefill: the first 512 queries of request 0, `threads` heads
+    nq, nh = 512, min(threads, H)
+    idx = torch.as_tensor(wl.lay.block_tables[0, :nq // 16]).cuda()
+    kk, vv = host_bf16(kp[idx]), host_bf16(vp[idx])
+    qq = host_bf16(wl.full["q"][:nq])
+    t0 = time.time()
+    ref.paged_attention(qq, kk, vv, np.arange(nq // 16, dtype=np.int32)[None], [nq], [0, nq],
+                        D ** -0.5, units=[(0, h) for h in range(nh)], threads=threads)
+    rates["paged_prefill_head_pairs_per_s"] = nh * nq * (nq + 1) // 2 / (time.time() - t0)
+    # extrapolate one whole step
+    dec_keys = int(wl.ctx[wl.n_p:].astype(np.int64).sum())
+    step_s = (wl.n_lin * (wl.n_p * H / rates["linear_prefill_units_per_s"]
+                          + wl.n_d * H / rates["linear_decode_units_per_s"])
+              + wl.n_full * (H * dec_keys / rates["paged_decode_head_keys_per_s"]
+                             + wl.n_p * H * (P * (P + 1) // 2) / rates["paged_prefill_head_pairs_per_s"]))
+    return dict(value=round(wl.tokens / step_s, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample=(f"fp64 oracle, {threads} threads, on sampled units of the same step: "
+                        f"{nu} linear-prefill (request, head) units of 4096 tokens, {nr * H} "
+                        "linear-decode units, 4 paged-decode requests (all heads and keys), "
+                        f"512-query causal prefill x {nh} heads; measured rates extrapolated "
+                        "to the whole step"),
+                extrapolated_step_s=round(step_s, 1),
+                rates={k: round(v, 2) for k, v in rates.items()})
+
+
+# --------------------------------------------------------------------- main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--ctx-scale", type=float, default=1.0,
+                    help="scale of the longest decode context (1.0 = 131072)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the hybrid attention step has no multi-GPU path here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from linear_attention_attn_amd import hyattn as hy
+    hy.load()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {props.gcnArchName} CUs={props.multi_processor_count} "
+        f"mem={props.total_memory / 2**30:.0f} GiB")
+    wl = Workload(args.ctx_scale)
+    st = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        wl.step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    e0.record(st)
+    for _ in range(args.steps):
+        wl.step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f}s)")
+    value = wl.tokens / (ms * 1e-3)
+    out = {
+        "metric": "hybrid attn tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "hybrid 32-layer attention step (24 linear : 8 full), H=32, "
+                               "H_kv=8, D=128, 16x4096-token chunked prefill + 240 decode, "
+                               "contexts log-uniform to 131072, 16-token KV blocks, fp32 states",
+                   "global_batch": wl.n_p + wl.n_d, "tokens_per_step": wl.tokens,
+                   "layers": len(wl.types), "chunk": W["chunk"], "seq_len": W["prefill_len"],
+                   "max_context": wl.max_context, "parallelism": "none (1 GPU)"},
+    }
+    roof = dominant_kernel_roofline(wl, max(1, min(args.steps, 3)))
+    log(f"dominant kernel: {roof}")
+    out["roofline"] = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    out["roofline"]["kernel"] = roof["kernel"]
+    if not args.no_components:
+        comp = component_times(wl)
+        n_lin, n_full = wl.n_lin, wl.n_full
+        lp, ld, pd = comp["linear_prefill"], comp["linear_decode"], comp["paged_decode"]
+        out["components_ms_per_call"] = {k: round(v, 4) for k, v in comp.items()}
+        out["components"] = {
+            "linear_decode_hbm_frac": round(wl.linear_decode_bytes() / (ld * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "paged_decode_hbm_frac": round(wl.decode_kv_bytes() / (pd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "linear_prefill_mfma_frac": round(wl.linear_prefill_flops() / (lp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "linear_prefill_hbm_frac": round(wl.linear_prefill_bytes() / (lp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "paged_prefill_mfma_frac": round(wl.paged_prefill_flops() / (comp["paged_prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "step_ms_from_components": round(comp["state_zero"] + n_lin * (lp + ld) + n_full * (
+                comp["paged_append"] + comp["paged_prefill"] + pd), 3),
+        }
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl)
+        log(f"cpu baseline took {time.time() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -434,6 +434,211 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   return hipGetLastError();
 }
 
+// ============================================================================
+// Causal prefill, bf16 (MFMA, FlashAttention-style). grid (query tiles, H_kv,
+// B), 4 waves. A workgroup takes QT = 256 / G query positions of one request
+// for all G query heads sharing KV head g (256 rows), so every K/V tile staged
+// in LDS serves G heads. Wave w owns 64 rows (4 tiles of 16).
+//
+// Per 64-key stage (4 blocks gathered through the block table, K row-major
+// and V transposed in LDS, double-buffered with the next stage's global loads
+// in flight) and per 32-key half:
+//   S^T = K Q^T   (two 16-key tiles; the key order inside each tile is
+//                  permuted so that a lane ends up with 8 consecutive keys of
+//                  its row, i.e. directly the B operand below)
+//   online softmax over the lane's row (max via two cross-row shuffles)
+//   O^T += V^T P^T (A = V^T fragment from LDS, B = P^T from registers)
+// Computing O^T rather than O keeps the softmax row, the score column and the
+// output column on the same lane, so rescaling needs no data movement.
+// ============================================================================
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_paged_prefill_bf16(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
+    int H_kv, float scale_log2) {
+  constexpr int QT = 256 / G;   // query positions per workgroup
+  constexpr int NR = 4;         // 16-row tiles per wave
+  constexpr int KS = D / 32;    // k steps over the head dim
+  constexpr int NDT = D / 16;   // 16-wide head-dim tiles of O^T
+  constexpr int KT = 64;        // keys per LDS stage
+  constexpr int KRS = D + 8;    // K tile row stride (elements)
+  constexpr int VRS = KT + 8;   // V^T tile row stride (elements)
+  constexpr int CG = D / 8;     // 16-byte column groups of a K/V row
+  constexpr int TGN = 256 / CG; // 4-token groups per staging pass
+  __shared__ __align__(16) uint16_t Ks[2][KT * KRS];
+  __shared__ __align__(16) uint16_t Vt[2][D * VRS];
+
+  const int qtile = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int q0 = cu_q[r], ql = cu_q[r + 1] - q0;
+  const int i0 = qtile * QT;
+  if (i0 >= ql) return;
+  const int c = min(ctx[r], max_blocks * kBlock);
+  const int base_pos = c - ql;  // position of this request's first query
+  if (base_pos < 0) return;     // more queries than context: invalid input
+  const int kend = min(c, base_pos + i0 + QT);
+  const int n_st = (kend + KT - 1) / KT;
+  const int32_t* btr = bt + (int64_t)r * max_blocks;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+
+  // ---- rows of this lane: tile rt covers wave rows 16 rt .. 16 rt + 15 ----
+  int row_pos[NR];   // query position inside the request (may be >= ql: padding)
+  int row_head[NR];
+  u32x4 qf[NR][KS];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    const int R = w * 64 + 16 * rt + lr;
+    row_head[rt] = R / QT;
+    row_pos[rt] = i0 + R % QT;
+    const bool ok = row_pos[rt] < ql;
+    const uint16_t* qp = q + ((int64_t)(q0 + row_pos[rt]) * H_q + g * G + row_head[rt]) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x4 ot[NDT][NR];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NR], l_run[NR];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
+
+  // ---- staging: thread -> (4 tokens, 8 head dims) of the stage ----
+  const int sdg = tid % CG, stg = tid / CG;
+  const bool stager = 4 * stg < KT;
+  u32x4 pk[4], pv[4];
+  auto load_stage = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = st * KT + 4 * stg + i;
+      pk[i] = u32x4{0u, 0u, 0u, 0u};
+      pv[i] = pk[i];
+      if (stager && key < c) {
+        const int32_t blk = btr[key >> 4];
+        if (blk >= 0 && blk < n_blocks) {
+          const int64_t off = (((int64_t)blk * H_kv + g) * kBlock + (key & 15)) * D + 8 * sdg;
+          pk[i] = *reinterpret_cast<const u32x4*>(k_pool + off);
+          pv[i] = *reinterpret_cast<const u32x4*>(v_pool + off);
+        }
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    if (!stager) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&Ks[buf][(4 * stg + i) * KRS + 8 * sdg]) = pk[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x2 t;
+      t[0] = ((pv[0][j >> 1] >> (16 * (j & 1))) & 0xffffu) | (((pv[1][j >> 1] >> (16 * (j & 1))) & 0xffffu) << 16);
+      t[1] = ((pv[2][j >> 1] >> (16 * (j & 1))) & 0xffffu) | (((pv[3][j >> 1] >> (16 * (j & 1))) & 0xffffu) << 16);
+      *reinterpret_cast<u32x2*>(&Vt[buf][(8 * sdg + j) * VRS + 4 * stg]) = t;
+    }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < n_st; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < n_st) load_stage(st + 1);
+    const uint16_t* Kb = Ks[buf];
+    const uint16_t* Vb = Vt[buf];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int key0 = st * KT + 32 * kk;
+      if (key0 >= kend) break;
+      // ---- scores S^T for 32 keys x this wave's 64 rows ----
+      f32x4 sc[2][NR];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int krow = 32 * kk + 8 * (lr >> 2) + 4 * u + (lr & 3);
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) sc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(Kb + krow * KRS + 32 * s + 8 * lg);
+#pragma unroll
+          for (int rt = 0; rt < NR; ++rt) sc[u][rt] = mfma16x16x32(kf, qf[rt][s], sc[u][rt]);
+        }
+      }
+      // ---- online softmax per row; lane holds keys key0 + 8 lg + 4u + i ----
+      u32x4 pb[NR];
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) {
+        const int pos = base_pos + row_pos[rt];
+        float x[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 8 * lg + 4 * u + i;
+            const float v = (key <= pos) ? sc[u][rt][i] * scale_log2 : -INFINITY;
+            x[4 * u + i] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m_run[rt], mx);
+        const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - mn);
+        m_run[rt] = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x[j] = (mn == -INFINITY) ? 0.f : fast_exp2(x[j] - mn);
+          ps += x[j];
+        }
+        l_run[rt] = l_run[rt] * corr + ps;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          ot[dt][rt][0] *= corr;
+          ot[dt][rt][1] *= corr;
+          ot[dt][rt][2] *= corr;
+          ot[dt][rt][3] *= corr;
+        }
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) pb[rt][p2] = pack_bf16x2(x[2 * p2], x[2 * p2 + 1]);
+      }
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(Vb + (16 * dt + lr) * VRS + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf, pb[rt], ot[dt][rt]);
+      }
+    }
+    if (st + 1 < n_st) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds O^T[d = 16 dt + 4 lg + i][row lr] ----
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    float L = l_run[rt];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const float inv = 1.f / L;
+    if (row_pos[rt] >= ql) continue;
+    uint16_t* op = o + ((int64_t)(q0 + row_pos[rt]) * H_q + g * G + row_head[rt]) * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x2 t;
+      t[0] = pack_bf16x2(ot[dt][rt][0] * inv, ot[dt][rt][1] * inv);
+      t[1] = pack_bf16x2(ot[dt][rt][2] * inv, ot[dt][rt][3] * inv);
+      *reinterpret_cast<u32x2*>(op + 16 * dt) = t;
+    }
+  }
+}
+
 hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
                                 int64_t n_blocks, const int32_t* bt, int max_blocks,
                                 const int32_t* ctx,
@@ -442,11 +647,30 @@ hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, cons
   if (B <= 0 || max_q_len <= 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (bf16) {
-    if (D == 128)
-      return launch_simple<128, uint16_t>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q,
-                                          max_q_len, B, H_q, H_kv, sl2, s);
-    return launch_simple<64, uint16_t>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q, max_q_len,
-                                       B, H_q, H_kv, sl2, s);
+    const int G = H_q / H_kv;
+#define HY_PP(DD, GG)                                                                          \
+  do {                                                                                         \
+    dim3 grid((unsigned)((max_q_len + (256 / GG) - 1) / (256 / GG)), (unsigned)H_kv, (unsigned)B); \
+    hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG>), grid, dim3(256), 0, s, (const uint16_t*)q, \
+                       (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
+                       bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2);                             \
+  } while (0)
+#define HY_PP_G(DD)                   \
+  switch (G) {                        \
+    case 1: HY_PP(DD, 1); break;      \
+    case 2: HY_PP(DD, 2); break;      \
+    case 4: HY_PP(DD, 4); break;      \
+    case 8: HY_PP(DD, 8); break;      \
+    default: return hipErrorInvalidValue; \
+  }
+    if (D == 128) {
+      HY_PP_G(128)
+    } else {
+      HY_PP_G(64)
+    }
+#undef HY_PP_G
+#undef HY_PP
+    return hipGetLastError();
   }
   if (D == 128)
     return launch_simple<128, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q, max_q_len,
