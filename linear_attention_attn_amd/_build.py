@@ -34,6 +34,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC]
 
 
+# Extra flags per source. The paged kernels keep MFMA results in ordinary VGPRs:
+# their scores feed VALU softmax code, and the default placement in AGPRs
+# costs a copy per use.
+PER_FILE = {"k_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -46,7 +52,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *COMMON, *lang, "-c", src, "-o", obj]
+        extra = PER_FILE.get(os.path.basename(src), [])
+        cmd = [cc, *COMMON, *extra, *lang, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

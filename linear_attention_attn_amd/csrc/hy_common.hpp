@@ -17,22 +17,22 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Split x into hi + lo, both bf16, with hi = RNE(x) and lo = RNE(x - hi).
-// hi + lo reproduces x to about 2^-17 relative.
-__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_bits(x);
-  lo = f32_to_bf16_bits(x - __uint_as_float(hi << 16));
+// Round two floats to bf16, nearest-even (one v_cvt_pk_bf16_f32); the first
+// lands in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// Split a pair into hi + lo bf16 pairs: hi = RNE(x), lo = RNE(x - hi); hi + lo
+// reproduces x to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
 }
 
 // ---- element I/O --------------------------------------------------------------

@@ -237,11 +237,10 @@ __device__ __forceinline__ uint32_t bf16_elem(u32x4 r, int j) {
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    uint32_t h0, l0, h1, l1;
-    split_bf16(x[2 * p], h0, l0);
-    split_bf16(x[2 * p + 1], h1, l1);
-    hi[p] = h0 | (h1 << 16);
-    lo[p] = l0 | (l1 << 16);
+    uint32_t h, l;
+    split_bf16x2(x[2 * p], x[2 * p + 1], h, l);
+    hi[p] = h;
+    lo[p] = l;
   }
 }
 

@@ -19,6 +19,8 @@
 namespace hy {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.f;  // log2 headroom before the softmax reference moves
+constexpr int kPrefillNR = 2;    // 16-row tiles per wave in causal prefill
 
 // ============================================================================
 // Append: copy each new token's K and V rows into its slot. grid (token tiles
@@ -72,209 +74,265 @@ hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_poo
 
 // ============================================================================
 // Decode planning: a request's context is split into partitions of
-// part_blocks blocks; each (request, KV head, partition) is one workgroup and
-// the partial results are merged by log-sum-exp.
+// part_blocks blocks (a multiple of 16 blocks = one pass of a workgroup, at
+// most kMaxParts partitions for the longest context). Work items are the
+// (request, partition) pairs; k_decode_plan lays them out with an exclusive
+// scan, so the attention grid never holds empty workgroups.
 // ============================================================================
-constexpr int kMinPartBlocks = 32;  // 512 tokens
+constexpr int kPassBlocks = 16;  // blocks per workgroup pass (4 waves x 4 blocks)
 constexpr int kMaxParts = 64;
 
 DecodePlan decode_plan(int max_context) {
   const int nblk = (max_context + kBlock - 1) / kBlock;
   int pb = (nblk + kMaxParts - 1) / kMaxParts;
-  if (pb < kMinPartBlocks) pb = kMinPartBlocks;
+  pb = ((pb + kPassBlocks - 1) / kPassBlocks) * kPassBlocks;
+  if (pb < kPassBlocks) pb = kPassBlocks;
   int parts = (nblk + pb - 1) / pb;
   if (parts < 1) parts = 1;
   return DecodePlan{pb, parts};
 }
 
+static size_t decode_partials_bytes(int B, int H_q, int D, int max_parts) {
+  const size_t b = (size_t)B * H_q * max_parts * (size_t)(D + 2) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
+}
+
 size_t decode_workspace_bytes(int B, int H_q, int D, int max_context) {
   const DecodePlan p = decode_plan(max_context);
-  return (size_t)B * H_q * p.max_parts * (size_t)(D + 2) * sizeof(float);
+  return decode_partials_bytes(B, H_q, D, p.max_parts) + ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+__device__ __forceinline__ int n_parts_of(int c, int max_blocks, int part_blocks, int max_parts) {
+  c = min(c, max_blocks * kBlock);  // defensive: never read past the table
+  const int nblk = (max(c, 0) + kBlock - 1) / kBlock;
+  return min((nblk + part_blocks - 1) / part_blocks, max_parts);
+}
+
+// One workgroup of 1024 threads: cu_parts[r] = sum of partitions of requests < r.
+__global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict__ ctx, int B,
+                                                      int max_blocks, int part_blocks,
+                                                      int max_parts, int32_t* __restrict__ cu_parts) {
+  __shared__ int32_t sums[1024];
+  const int t = threadIdx.x;
+  const int per = (B + 1023) / 1024;
+  const int r0 = min(B, t * per), r1 = min(B, r0 + per);
+  int acc = 0;
+  for (int r = r0; r < r1; ++r) acc += n_parts_of(ctx[r], max_blocks, part_blocks, max_parts);
+  sums[t] = acc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? sums[t - off] : 0;
+    __syncthreads();
+    sums[t] += v;
+    __syncthreads();
+  }
+  int base = t ? sums[t - 1] : 0;
+  for (int r = r0; r < r1; ++r) {
+    cu_parts[r] = base;
+    base += n_parts_of(ctx[r], max_blocks, part_blocks, max_parts);
+  }
+  if (t == 1023) cu_parts[B] = sums[1023];
 }
 
 // ============================================================================
-// Decode, bf16 (MFMA scores). grid (max_parts, H_kv, B), 4 waves.
+// Decode, bf16. grid (workers, H_kv), 4 waves; each workgroup walks the
+// (request, partition) items worker, worker + gridDim.x, ... for KV head g.
 //
-// Each wave takes every 4th block of the partition. Scores of the G query
-// heads sharing KV head g against the block's 16 keys come from four
-// v_mfma_f32_16x16x32_bf16 (A = the 16 K rows, B = the query heads padded to
-// 16 columns); lane l then holds keys 4*(l/16)+i of head l%16. For P.V the
-// lane owns value dims DPL*(l%16) .. +DPL of keys 4*(l/16)+i, so the weights
-// it needs sit in its own 16-lane row and are fetched with shuffles.
+// A partition is processed in passes of 16 blocks; in a pass, wave w issues
+// the loads of its 4 blocks (32 KiB of K and V) at once. Scores of the G query
+// heads sharing KV head g come from v_mfma_f32_16x16x32_bf16 (A = the 16 K
+// rows of a block, B = the query heads padded to 16 columns): lane l holds
+// keys 4*(l/16)+i of head l%16. Weights go through LDS to the P.V lanes, which
+// own DPL = D/16 value dims of keys 4*(l/16)+i of each block. Every wave keeps
+// an online softmax; the 4 waves are merged by log-sum-exp at the end.
 // ============================================================================
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_paged_decode_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
-    int max_blocks, const int32_t* __restrict__ ctx, int H_q, int H_kv, float scale_log2,
-    int part_blocks, int max_parts, float* __restrict__ ws) {
+    int max_blocks, const int32_t* __restrict__ ctx, int B, int H_q, int H_kv, float scale_log2,
+    int part_blocks, int max_parts, float* __restrict__ ws, const int32_t* __restrict__ cu_parts) {
   constexpr int KS = D / 32;    // k steps of the score MFMA
   constexpr int DPL = D / 16;   // value dims per lane in P.V
   constexpr int NW = 4;
-  const int part = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int c = min(ctx[r], max_blocks * kBlock);  // defensive: never read past the table
-  const int nblk = (c + kBlock - 1) / kBlock;
-  const int n_parts = min((nblk + part_blocks - 1) / part_blocks, max_parts);
-  if (part >= n_parts) return;
-  const int b_begin = part * part_blocks;
-  const int b_end = min(nblk, b_begin + part_blocks);
+  constexpr int BPW = 4;        // blocks per wave per pass
+  __shared__ __align__(16) float s_p[NW][G][BPW * kBlock];
+  __shared__ float s_corr[NW][G];
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ __align__(16) float s_acc[NW][G][D];
 
+  const int g = blockIdx.y;
+  const int total = cu_parts[B];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-  const int h0 = g * G;
-
-  // query fragment (B operand): column lr = head h0 + lr (zero beyond G)
-  u32x4 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (lr < G)
-      qf[s] = *reinterpret_cast<const u32x4*>(q + ((int64_t)r * H_q + h0 + lr) * D + 32 * s + 8 * lg);
-    else
-      qf[s] = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  float m_all[G], l_part[G], acc[G][DPL];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m_all[hh] = -INFINITY;
-    l_part[hh] = 0.f;
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
-  }
-  float m_own = -INFINITY;  // running max of head lr (lanes lr < G)
-
-  const int32_t* btr = bt + (int64_t)r * max_blocks;
   const int64_t head_stride = (int64_t)kBlock * D;
 
-  for (int b = b_begin + w; b < b_end; b += NW) {
-    const int32_t blk = btr[b];
-    if (blk < 0 || blk >= n_blocks) continue;  // defensive: invalid ids are skipped
-    const int64_t base = ((int64_t)blk * H_kv + g) * head_stride;
-    const uint16_t* kblk = k_pool + base;
-    const uint16_t* vblk = v_pool + base;
-    u32x4 kf[KS];
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    int lo = 0, hi = B;  // cu_parts[lo] <= item < cu_parts[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_parts[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int r = lo;
+    const int part = item - cu_parts[r];
+    const int c = min(ctx[r], max_blocks * kBlock);
+    const int nblk = (c + kBlock - 1) / kBlock;
+    const int n_parts = n_parts_of(c, max_blocks, part_blocks, max_parts);
+    const int b_begin = part * part_blocks;
+    const int b_end = min(nblk, b_begin + part_blocks);
+    const int h0 = g * G;
+    const int32_t* btr = bt + (int64_t)r * max_blocks;
+
+    u32x4 qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      kf[s] = *reinterpret_cast<const u32x4*>(kblk + lr * D + 32 * s + 8 * lg);
-    // value rows 4*lg + i, dims DPL*lr .. +DPL
-    uint32_t vr[4][DPL / 2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* vp = vblk + (4 * lg + i) * D + DPL * lr;
-      if constexpr (DPL == 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vp);
-        vr[i][0] = x[0]; vr[i][1] = x[1]; vr[i][2] = x[2]; vr[i][3] = x[3];
-      } else {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
-        vr[i][0] = x[0]; vr[i][1] = x[1];
-      }
-    }
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) sc = mfma16x16x32(kf[s], qf[s], sc);
-
-    // scores: key 16b + 4*lg + i of head lr
-    float x[4];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool valid = 16 * b + 4 * lg + i < c;
-      x[i] = valid ? sc[i] * scale_log2 : -INFINITY;
-      bm = fmaxf(bm, x[i]);
-    }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_own_new = fmaxf(m_own, bm);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_own_new);
-    m_own = m_own_new;
-
-    float corr[G];
+      qf[s] = lr < G ? *reinterpret_cast<const u32x4*>(q + ((int64_t)r * H_q + h0 + lr) * D + 32 * s + 8 * lg)
+                     : u32x4{0u, 0u, 0u, 0u};
+    float l_part[G], acc[G][DPL];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float bmh = __shfl(bm, hh);
-      const float mn = fmaxf(m_all[hh], bmh);
-      corr[hh] = fast_exp2(m_all[hh] - mn);
-      m_all[hh] = mn;
+      l_part[hh] = 0.f;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
     }
-    // values of keys beyond the context are masked (the pool may hold junk there)
-    bool vvalid[4];
+    float m_own = -INFINITY;  // running max of head lr (lanes lr < G), scaled domain
+
+    for (int p0 = b_begin; p0 < b_end; p0 += NW * BPW) {
+      // ---- issue all loads of this wave's blocks ----
+      u32x4 kf[BPW][KS];
+      uint32_t vr[BPW][4][DPL / 2];
+      int ntok[BPW];  // valid tokens of each block (0 if absent)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vvalid[i] = 16 * b + 4 * lg + i < c;
+      for (int j = 0; j < BPW; ++j) {
+        const int b = p0 + w * BPW + j;
+        int32_t blk = b < b_end ? btr[b] : -1;
+        if (blk >= n_blocks) blk = -1;  // defensive: invalid ids are skipped
+        ntok[j] = blk >= 0 ? min(kBlock, c - kBlock * b) : 0;
+        const int64_t base = ((int64_t)(blk < 0 ? 0 : blk) * H_kv + g) * head_stride;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float ph[4];
+        for (int s = 0; s < KS; ++s)
+          kf[j][s] = blk >= 0 ? *reinterpret_cast<const u32x4*>(k_pool + base + lr * D + 32 * s + 8 * lg)
+                              : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ph[i] = __shfl(p[i], 16 * lg + hh);
-      float ls = l_part[hh] * corr[hh];
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr[hh];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!vvalid[i]) continue;
-        ls += ph[i];
-#pragma unroll
-        for (int d2 = 0; d2 < DPL / 2; ++d2) {
-          acc[hh][2 * d2] = __builtin_fmaf(ph[i], bf16_lo(vr[i][d2]), acc[hh][2 * d2]);
-          acc[hh][2 * d2 + 1] = __builtin_fmaf(ph[i], bf16_hi(vr[i][d2]), acc[hh][2 * d2 + 1]);
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t* vp = v_pool + base + (4 * lg + i) * D + DPL * lr;
+          if constexpr (DPL == 8) {
+            const u32x4 x = blk >= 0 ? *reinterpret_cast<const u32x4*>(vp) : u32x4{0u, 0u, 0u, 0u};
+            vr[j][i][0] = x[0]; vr[j][i][1] = x[1]; vr[j][i][2] = x[2]; vr[j][i][3] = x[3];
+          } else {
+            const u32x2 x = blk >= 0 ? *reinterpret_cast<const u32x2*>(vp) : u32x2{0u, 0u};
+            vr[j][i][0] = x[0]; vr[j][i][1] = x[1];
+          }
         }
       }
-      l_part[hh] = ls;
+      // ---- scores: lane holds key 4*lg + i of block j for head lr ----
+      float x[BPW][4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sc = mfma16x16x32(kf[j][s], qf[s], sc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[j][i] = (4 * lg + i < ntok[j]) ? sc[i] * scale_log2 : -INFINITY;
+          bm = fmaxf(bm, x[j][i]);
+        }
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m_own, bm);
+      const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+      if (lr < G) {
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          f32x4 pv4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv4[i] = fast_exp2(x[j][i] - mref);
+          *reinterpret_cast<f32x4*>(&s_p[w][lr][j * kBlock + 4 * lg]) = pv4;
+        }
+        if (lg == 0) s_corr[w][lr] = (m_own == -INFINITY) ? 0.f : fast_exp2(m_own - mref);
+      }
+      m_own = m_new;
+      __syncthreads();
+      // ---- P.V: lane owns dims DPL*lr .. +DPL of keys 4*lg + i of each block ----
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float corr = s_corr[w][hh];
+        float ls = l_part[hh] * corr;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr;
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[w][hh][j * kBlock + 4 * lg]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // keys beyond the context have weight 0; their values may be junk
+            const bool ok = 4 * lg + i < ntok[j];
+            const float pw = ok ? p4[i] : 0.f;
+            ls += pw;
+#pragma unroll
+            for (int d2 = 0; d2 < DPL / 2; ++d2) {
+              const uint32_t vv = ok ? vr[j][i][d2] : 0u;
+              acc[hh][2 * d2] = __builtin_fmaf(pw, bf16_lo(vv), acc[hh][2 * d2]);
+              acc[hh][2 * d2 + 1] = __builtin_fmaf(pw, bf16_hi(vv), acc[hh][2 * d2 + 1]);
+            }
+          }
+        }
+        l_part[hh] = ls;
+      }
+      __syncthreads();  // s_p / s_corr are rewritten by the next pass
     }
-  }
 
-  // ---- combine the 4 token rows of the wave (same running max) ----
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    l_part[hh] += __shfl_xor(l_part[hh], 16);
-    l_part[hh] += __shfl_xor(l_part[hh], 32);
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) {
-      acc[hh][d] += __shfl_xor(acc[hh][d], 16);
-      acc[hh][d] += __shfl_xor(acc[hh][d], 32);
-    }
-  }
-  // ---- combine the 4 waves ----
-  __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_acc[NW][G][D];
-  if (l < 16) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) s_acc[w][hh][DPL * lr + d] = acc[hh][d];
-  }
-  if (l == 0) {
+    // ---- combine the 4 token rows of the wave (same running max) ----
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      s_m[w][hh] = m_all[hh];
-      s_l[w][hh] = l_part[hh];
-    }
-  }
-  __syncthreads();
-  const bool single = (n_parts == 1);
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D, d = idx - (idx / D) * D;
-    float M = -INFINITY;
+      l_part[hh] += __shfl_xor(l_part[hh], 16);
+      l_part[hh] += __shfl_xor(l_part[hh], 32);
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][hh]);
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = (s_m[ww][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][hh] - M);
-      L += s_l[ww][hh] * f;
-      A += s_acc[ww][hh][d] * f;
-    }
-    const int head = h0 + hh;
-    if (single) {
-      o[((int64_t)r * H_q + head) * D + d] = (uint16_t)f32_to_bf16_bits(A / L);
-    } else {
-      float* wp = ws + (((int64_t)r * H_q + head) * max_parts + part) * (D + 2);
-      wp[2 + d] = A;
-      if (d == 0) {
-        wp[0] = M;
-        wp[1] = L;
+      for (int d = 0; d < DPL; ++d) {
+        acc[hh][d] += __shfl_xor(acc[hh][d], 16);
+        acc[hh][d] += __shfl_xor(acc[hh][d], 32);
       }
     }
+    // ---- combine the 4 waves ----
+    if (l < 16) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) s_acc[w][hh][DPL * lr + d] = acc[hh][d];
+    }
+    if (l < G) s_m[w][l] = m_own;
+    if (l == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) s_l[w][hh] = l_part[hh];
+    }
+    __syncthreads();
+    const bool single = (n_parts == 1);
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int hh = idx / D, d = idx - (idx / D) * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][hh]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = (s_m[ww][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][hh] - M);
+        L += s_l[ww][hh] * f;
+        A += s_acc[ww][hh][d] * f;
+      }
+      const int head = h0 + hh;
+      if (single) {
+        o[((int64_t)r * H_q + head) * D + d] = (uint16_t)f32_to_bf16_bits(L > 0.f ? A / L : 0.f);
+      } else {
+        float* wp = ws + (((int64_t)r * H_q + head) * max_parts + part) * (D + 2);
+        wp[2 + d] = A;
+        if (d == 0) {
+          wp[0] = M;
+          wp[1] = L;
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next item
   }
 }
 
@@ -289,9 +347,7 @@ __global__ void k_paged_merge(T* __restrict__ o, const int32_t* __restrict__ ctx
                               const float* __restrict__ ws) {
   const int rh = blockIdx.x;
   const int r = rh / H_q;
-  const int c = min(ctx[r], max_blocks * kBlock);
-  const int nblk = (c + kBlock - 1) / kBlock;
-  const int n_parts = min((nblk + part_blocks - 1) / part_blocks, max_parts);
+  const int n_parts = n_parts_of(ctx[r], max_blocks, part_blocks, max_parts);
   if (n_parts == 1) return;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float out = 0.f;
@@ -301,11 +357,11 @@ __global__ void k_paged_merge(T* __restrict__ o, const int32_t* __restrict__ ctx
       for (int p = 0; p < n_parts; ++p) M = fmaxf(M, wp[p * (D + 2)]);
       float L = 0.f, A = 0.f;
       for (int p = 0; p < n_parts; ++p) {
-        const float f = fast_exp2(wp[p * (D + 2)] - M);
+        const float f = (wp[p * (D + 2)] == -INFINITY) ? 0.f : fast_exp2(wp[p * (D + 2)] - M);
         L += wp[p * (D + 2) + 1] * f;
         A += wp[p * (D + 2) + 2 + d] * f;
       }
-      out = A / L;
+      out = L > 0.f ? A / L : 0.f;
     }
     io<T>::st(o, (int64_t)rh * D + d, out);
   }
@@ -406,11 +462,21 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   const DecodePlan plan = decode_plan(max_context);
   const int G = H_q / H_kv;
   float* ws = (float*)workspace;
-  dim3 grid((unsigned)plan.max_parts, (unsigned)H_kv, (unsigned)B), block(256);
+  int32_t* cu_parts = reinterpret_cast<int32_t*>(
+      (char*)workspace + decode_partials_bytes(B, H_q, D, plan.max_parts));
+  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, s, ctx, B, max_blocks,
+                     plan.part_blocks, plan.max_parts, cu_parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // enough workers to fill the chip a few times over; each walks items with stride gridDim.x
+  const long bound = (long)B * plan.max_parts;
+  const unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
+  dim3 grid(workers, (unsigned)H_kv), block(256);
 #define HY_PD(DD, GG)                                                                         \
   hipLaunchKernelGGL((k_paged_decode_bf16<DD, GG>), grid, block, 0, s, (const uint16_t*)q,    \
                      (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
-                     bt, max_blocks, ctx, H_q, H_kv, sl2, plan.part_blocks, plan.max_parts, ws)
+                     bt, max_blocks, ctx, B, H_q, H_kv, sl2, plan.part_blocks, plan.max_parts, \
+                     ws, cu_parts)
 #define HY_PD_G(DD)                   \
   switch (G) {                        \
     case 1: HY_PD(DD, 1); break;      \
@@ -426,7 +492,7 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   }
 #undef HY_PD_G
 #undef HY_PD
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // partials of multi-partition requests are merged; empty contexts get zeros
   hipLaunchKernelGGL(k_paged_merge<uint16_t>, dim3((unsigned)(B * H_q)), dim3(D), 0, s,
@@ -436,9 +502,9 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 
 // ============================================================================
 // Causal prefill, bf16 (MFMA, FlashAttention-style). grid (query tiles, H_kv,
-// B), 4 waves. A workgroup takes QT = 256 / G query positions of one request
-// for all G query heads sharing KV head g (256 rows), so every K/V tile staged
-// in LDS serves G heads. Wave w owns 64 rows (4 tiles of 16).
+// B), 4 waves. A workgroup takes QT = 64 NR / G query positions of one request
+// for all G query heads sharing KV head g (64 NR rows), so every K/V tile
+// staged in LDS serves G heads. Wave w owns 16 NR rows (NR tiles of 16).
 //
 // Per 64-key stage (4 blocks gathered through the block table, K row-major
 // and V transposed in LDS, double-buffered with the next stage's global loads
@@ -451,14 +517,14 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 // Computing O^T rather than O keeps the softmax row, the score column and the
 // output column on the same lane, so rescaling needs no data movement.
 // ============================================================================
-template <int D, int G>
+template <int D, int G, int NR>
 __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
     int H_kv, float scale_log2) {
-  constexpr int QT = 256 / G;   // query positions per workgroup
-  constexpr int NR = 4;         // 16-row tiles per wave
+  constexpr int ROWS = 64 * NR; // rows (query position, head) per workgroup: 4 waves x 16 NR
+  constexpr int QT = ROWS / G;  // query positions per workgroup
   constexpr int KS = D / 32;    // k steps over the head dim
   constexpr int NDT = D / 16;   // 16-wide head-dim tiles of O^T
   constexpr int KT = 64;        // keys per LDS stage
@@ -478,6 +544,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   if (base_pos < 0) return;     // more queries than context: invalid input
   const int kend = min(c, base_pos + i0 + QT);
   const int n_st = (kend + KT - 1) / KT;
+  const int pos_lo = base_pos + i0;  // smallest query position of the workgroup
   const int32_t* btr = bt + (int64_t)r * max_blocks;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
@@ -488,7 +555,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   u32x4 qf[NR][KS];
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
-    const int R = w * 64 + 16 * rt + lr;
+    const int R = w * 16 * NR + 16 * rt + lr;
     row_head[rt] = R / QT;
     row_pos[rt] = i0 + R % QT;
     const bool ok = row_pos[rt] < ql;
@@ -552,7 +619,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     if (st + 1 < n_st) load_stage(st + 1);
     const uint16_t* Kb = Ks[buf];
     const uint16_t* Vb = Vt[buf];
-#pragma unroll
+#pragma nounroll
     for (int kk = 0; kk < 2; ++kk) {
       const int key0 = st * KT + 32 * kk;
       if (key0 >= kend) break;
@@ -571,42 +638,61 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
         }
       }
       // ---- online softmax per row; lane holds keys key0 + 8 lg + 4u + i ----
+      // Scores stay unscaled until the exponent: p = 2^(s * scale_log2 - m),
+      // m in the scaled domain. The reference m moves only when a row's new
+      // maximum exceeds it by more than kRescale (then p <= 2^kRescale), so
+      // the accumulator rescale is rare and done under a wave-uniform branch.
+      const bool diag = key0 + 31 > pos_lo;  // some key may lie beyond some row
       u32x4 pb[NR];
+      float corr[NR];
+      bool any_rescale = false;
 #pragma unroll
       for (int rt = 0; rt < NR; ++rt) {
         const int pos = base_pos + row_pos[rt];
+        if (diag) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 8 * lg + 4 * u + i > pos) sc[u][rt][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
+                         fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * scale_log2;
+        corr[rt] = 1.f;
+        if (ms > m_run[rt] + kRescale) {
+          corr[rt] = fast_exp2(m_run[rt] - ms);  // 0 when m_run is -inf
+          l_run[rt] *= corr[rt];
+          m_run[rt] = ms;
+          any_rescale = true;
+        }
         float x[8];
-        float mx = -INFINITY;
+        float ps = 0.f;
+        const float mref = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];  // row with no key yet
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 8 * lg + 4 * u + i;
-            const float v = (key <= pos) ? sc[u][rt][i] * scale_log2 : -INFINITY;
-            x[4 * u + i] = v;
-            mx = fmaxf(mx, v);
+            const float e = fast_exp2(__builtin_fmaf(sc[u][rt][i], scale_log2, -mref));
+            x[4 * u + i] = e;
+            ps += e;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m_run[rt], mx);
-        const float corr = (mn == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - mn);
-        m_run[rt] = mn;
-        float ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x[j] = (mn == -INFINITY) ? 0.f : fast_exp2(x[j] - mn);
-          ps += x[j];
-        }
-        l_run[rt] = l_run[rt] * corr + ps;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          ot[dt][rt][0] *= corr;
-          ot[dt][rt][1] *= corr;
-          ot[dt][rt][2] *= corr;
-          ot[dt][rt][3] *= corr;
-        }
+        l_run[rt] += ps;
 #pragma unroll
         for (int p2 = 0; p2 < 4; ++p2) pb[rt][p2] = pack_bf16x2(x[2 * p2], x[2 * p2 + 1]);
+      }
+      if (__builtin_amdgcn_ballot_w64(any_rescale)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int rt = 0; rt < NR; ++rt) {
+            ot[dt][rt][0] *= corr[rt];
+            ot[dt][rt][1] *= corr[rt];
+            ot[dt][rt][2] *= corr[rt];
+            ot[dt][rt][3] *= corr[rt];
+          }
       }
       // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -650,8 +736,9 @@ hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, cons
     const int G = H_q / H_kv;
 #define HY_PP(DD, GG)                                                                          \
   do {                                                                                         \
-    dim3 grid((unsigned)((max_q_len + (256 / GG) - 1) / (256 / GG)), (unsigned)H_kv, (unsigned)B); \
-    hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG>), grid, dim3(256), 0, s, (const uint16_t*)q, \
+    constexpr int QT_ = 64 * kPrefillNR / GG;                                                  \
+    dim3 grid((unsigned)((max_q_len + QT_ - 1) / QT_), (unsigned)H_kv, (unsigned)B);           \
+    hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR>), grid, dim3(256), 0, s, (const uint16_t*)q, \
                        (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
                        bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2);                             \
   } while (0)

@@ -162,14 +162,16 @@ def test_append_bit_exact(hy, dtype):
     assert np.array_equal(gu.host(dv), ref.append_kv(vp, vn, lay.block_tables, ctx, cu))
 
 
-@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 8, 2), ("f32", 64, 4, 4),
-                                             ("bf16", 64, 4, 1)])
-def test_prefill_two_chunks_matches_oracle(hy, dtype, D, Hq, Hkv):
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,long", [
+    ("bf16", 128, 8, 2, False), ("f32", 64, 4, 4, False), ("bf16", 64, 4, 1, False),
+    ("bf16", 128, 4, 4, False), ("bf16", 128, 16, 2, False), ("bf16", 64, 4, 2, False),
+    ("bf16", 128, 8, 2, True)])
+def test_prefill_two_chunks_matches_oracle(hy, dtype, D, Hq, Hkv, long):
     """Causal prefill in two chunks: the second attends to the first through the table."""
     import torch
-    rng = np.random.default_rng(305 + D)
-    total = np.array([150, 33, 64], np.int32)
-    first = np.array([100, 16, 1], np.int32)
+    rng = np.random.default_rng(305 + D + Hq)
+    total = np.array([700, 33, 64] if long else [150, 33, 64], np.int32)
+    first = np.array([300, 16, 1] if long else [100, 16, 1], np.int32)
     lay = synth.paged_layout(rng, total, n_spare=2)
     kp, vp = _poisoned_pools(rng, lay, Hkv, D, dtype, fill_ctx=np.zeros(3, np.int32))
     dkp, dvp = gu.dev(kp), gu.dev(vp)
