@@ -58,6 +58,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
+// i receives element i % 4 of the 8-byte chunks addressed by source lanes
+// 4 j + i / 4 (j = 0..3) of its group. Hence if source lane s points at
+// X[row0 + s / 4][c(s % 4)] of a row-major bf16 matrix X, lane i gets
+// X[row0 + j][c(i / 4) + i % 4] for j = 0..3: four consecutive rows of one
+// column, i.e. a k-contiguous MFMA operand read from a row-major tile.
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)lds));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// 8 consecutive rows row0 + 8*(l/16) + 0..7 of column col_q(l%16 / 4) + l%4 of
+// a row-major bf16 tile (row stride rs elements) as a 16x16x32 MFMA operand:
+// two transposing reads; col_q is the lane's column base for its l%16 / 4.
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int rs, int row0, int col_q) {
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const uint16_t* p = tile + (row0 + 8 * g + (s >> 2)) * rs + col_q;
+  const u32x2 a = ds_read_tr16(p);
+  const u32x2 b = ds_read_tr16(p + 4 * rs);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -200,21 +200,26 @@ __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ 
 //
 // One workgroup (4 waves) per (request, head). Wave w owns the value columns
 // [w*D/4, (w+1)*D/4) of the state, kept in fp32 accumulator registers for the
-// whole request. Per chunk, the chunk's Q and K (row-major) and K^T, V^T
-// (token-contiguous) are staged in LDS, then each wave computes, for its
+// whole request. Per chunk, K and V are staged row-major in LDS (72 KiB at
+// C = 128, so two workgroups share a CU and hide each other's staging); Q
+// fragments come straight from global memory. Each wave computes, for its
 // value columns:
 //   O_c   = Q_c S  (S split into bf16 hi + lo, two MFMAs: fp32-faithful)
 //         + tril(Q_c K_c^T) V_c  (scores in fp32, split hi + lo likewise)
 //   S    += K_c^T V_c (accumulated straight into the fp32 state registers)
-// Index permutations keep every MFMA operand a contiguous 16-byte LDS read:
+// Token-contiguous operands (K^T rows, V columns) are read from the
+// row-major tiles with the transposing LDS read. Index permutations keep the
+// other operands contiguous 16-byte reads:
 //  * state rows: accumulator tile t, row m holds key dim
 //      pi(t, m) = 32*(t/2) + 8*(m/4) + 4*(t%2) + m%4
 //    so that tiles 2s and 2s+1 together give each lane the 8 consecutive key
-//    dims 32s + 8*(l/16) + 0..7 that the Q fragment holds;
+//    dims 32s + 8*(l/16) + 0..7 that its Q fragment holds;
 //  * score tiles: P^T = K Q^T over 32 keys as two 16-row tiles whose row m
 //    is key 8*(m/4) + 4u + m%4 (u = tile), so each lane ends up with the 8
 //    consecutive keys 8*(l/16) + 0..7 of one query row, i.e. directly the A
 //    operand of P V.
+// LDS rows are D + 16 elements long (a stride of 8 mod 32 dwords), which
+// spreads both the row reads and the transposing reads over all banks.
 // ============================================================================
 template <int D>
 struct PrefillCfg {
@@ -223,15 +228,11 @@ struct PrefillCfg {
   static constexpr int NDV = DVW / 16; // 16-wide value tiles per wave
   static constexpr int NDK = D / 16;   // 16-row key-dim tiles of the state
   static constexpr int KS = D / 32;    // 32-wide k steps over the head dim
-  static constexpr int RS = D + 8;     // row stride (elements) of Q/K tiles
+  static constexpr int RS = D + 16;    // LDS row stride (elements)
 };
 
 __device__ __forceinline__ int state_row(int t, int m) {
   return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
-}
-
-__device__ __forceinline__ uint32_t bf16_elem(u32x4 r, int j) {
-  return (r[j >> 1] >> (16 * (j & 1))) & 0xffffu;
 }
 
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
@@ -248,11 +249,11 @@ template <int D>
 size_t prefill_bf16_lds_bytes(int C) {
   using Cfg = PrefillCfg<D>;
   const int Cp = (C + 31) & ~31;
-  return (size_t)2 * Cp * Cfg::RS * 2 + (size_t)2 * D * (Cp + 8) * 2;
+  return (size_t)2 * Cp * Cfg::RS * 2;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_linear_prefill_bf16(
+__global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     float* __restrict__ states, int n_slots, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int C) {
@@ -267,11 +268,8 @@ __global__ __launch_bounds__(256) void k_linear_prefill_bf16(
   if (T <= 0 || slot < 0 || slot >= n_slots) return;
 
   const int Cp = (C + 31) & ~31;
-  const int RT = Cp + 8;  // row stride of the token-contiguous tiles
-  uint16_t* Qs = lds_h;
-  uint16_t* Ks = Qs + Cp * RS;
-  uint16_t* KT = Ks + Cp * RS;
-  uint16_t* VT = KT + D * RT;
+  uint16_t* Ks = lds_h;
+  uint16_t* Vs = Ks + Cp * RS;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int dv0 = w * Cfg::DVW;
@@ -294,7 +292,7 @@ __global__ __launch_bounds__(256) void k_linear_prefill_bf16(
   for (int c0 = 0; c0 < T; c0 += C) {
     const int n = (T - c0 < C) ? (T - c0) : C;
     __syncthreads();  // the previous chunk's tiles are no longer read
-    // ---- stage Q, K (row-major) and K^T, V^T (token-contiguous) ----
+    // ---- stage K and V row-major (rows past n are zero) ----
     {
       constexpr int CG = D / 8;         // 16-byte column groups per row
       constexpr int TGS = 256 / CG;     // 4-token groups per pass
@@ -302,71 +300,67 @@ __global__ __launch_bounds__(256) void k_linear_prefill_bf16(
       for (int slab = 0; slab < Cp; slab += 4 * TGS) {
         const int a0 = slab + 4 * tg;
         if (a0 >= Cp) continue;
-        u32x4 rq[4], rk[4], rv[4];
+        u32x4 rk[4], rv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int a = a0 + i;
           if (a < n) {
             const int64_t off = (int64_t)(c0 + a) * ldx + 8 * dk8;
-            rq[i] = *reinterpret_cast<const u32x4*>(qb + off);
             rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
             rv[i] = *reinterpret_cast<const u32x4*>(vb + off);
           } else {
-            rq[i] = u32x4{0u, 0u, 0u, 0u};
-            rk[i] = rq[i];
-            rv[i] = rq[i];
+            rk[i] = u32x4{0u, 0u, 0u, 0u};
+            rv[i] = rk[i];
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(Qs + (a0 + i) * RS + 8 * dk8) = rq[i];
           *reinterpret_cast<u32x4*>(Ks + (a0 + i) * RS + 8 * dk8) = rk[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          u32x2 pk, pv;
-          pk[0] = bf16_elem(rk[0], j) | (bf16_elem(rk[1], j) << 16);
-          pk[1] = bf16_elem(rk[2], j) | (bf16_elem(rk[3], j) << 16);
-          pv[0] = bf16_elem(rv[0], j) | (bf16_elem(rv[1], j) << 16);
-          pv[1] = bf16_elem(rv[2], j) | (bf16_elem(rv[3], j) << 16);
-          *reinterpret_cast<u32x2*>(KT + (8 * dk8 + j) * RT + a0) = pk;
-          *reinterpret_cast<u32x2*>(VT + (8 * dk8 + j) * RT + a0) = pv;
+          *reinterpret_cast<u32x4*>(Vs + (a0 + i) * RS + 8 * dk8) = rv[i];
         }
       }
     }
     __syncthreads();
 
-    // ---- snapshot S (state before this chunk) as bf16 hi/lo B operands ----
-    u32x4 Shi[KS][NDV], Slo[KS][NDV];
+    // ---- outputs, 16 query rows at a time ----
+    // The state registers are not updated before the last row tile, so the
+    // bf16 hi/lo B operands of Q S (the state before this chunk) are rebuilt
+    // from them per row tile instead of being kept live.
+    const int nrt = (n + 15) >> 4;
+    // Q fragments come from global memory one row tile ahead of their use
+    u32x4 qnext[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int nn = 0; nn < NDV; ++nn) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = Sacc[2 * s][nn][i];
-          x[4 + i] = Sacc[2 * s + 1][nn][i];
-        }
-        split8(x, Shi[s][nn], Slo[s][nn]);
-      }
-
-    // ---- outputs, 16 query rows at a time ----
-    const int nrt = (n + 15) >> 4;
+      qnext[s] = lr < n ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(c0 + lr) * ldx + 32 * s + 8 * lg)
+                        : u32x4{0u, 0u, 0u, 0u};
     for (int rt = 0; rt < nrt; ++rt) {
       const int row = 16 * rt + lr;
       u32x4 qf[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[s] = *reinterpret_cast<const u32x4*>(Qs + row * RS + 32 * s + 8 * lg);
+      for (int s = 0; s < KS; ++s) qf[s] = qnext[s];
+      if (rt + 1 < nrt) {
+        const int nrow = row + 16;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qnext[s] = nrow < n ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(c0 + nrow) * ldx + 32 * s + 8 * lg)
+                              : u32x4{0u, 0u, 0u, 0u};
+      }
       f32x4 Oacc[NDV];
 #pragma unroll
       for (int nn = 0; nn < NDV; ++nn) {
         Oacc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          Oacc[nn] = mfma16x16x32(qf[s], Shi[s][nn], Oacc[nn]);
-          Oacc[nn] = mfma16x16x32(qf[s], Slo[s][nn], Oacc[nn]);
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = Sacc[2 * s][nn][i];
+            x[4 + i] = Sacc[2 * s + 1][nn][i];
+          }
+          u32x4 shi, slo;
+          split8(x, shi, slo);
+          Oacc[nn] = mfma16x16x32(qf[s], shi, Oacc[nn]);
+          Oacc[nn] = mfma16x16x32(qf[s], slo, Oacc[nn]);
         }
       }
       const int nkb = (16 * rt + 15) / 32 + 1;
@@ -394,7 +388,7 @@ __global__ __launch_bounds__(256) void k_linear_prefill_bf16(
         split8(pv, phi, plo);
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(VT + (dv0 + 16 * nn + lr) * RT + 32 * kb32 + 8 * lg);
+          const u32x4 vf = tr_operand(Vs, RS, 32 * kb32, dv0 + 16 * nn + 4 * (lr & 3));
           Oacc[nn] = mfma16x16x32(phi, vf, Oacc[nn]);
           Oacc[nn] = mfma16x16x32(plo, vf, Oacc[nn]);
         }
@@ -414,11 +408,11 @@ __global__ __launch_bounds__(256) void k_linear_prefill_bf16(
     for (int ts = 0; ts < nts; ++ts) {
       u32x4 vf[NDV];
 #pragma unroll
-      for (int nn = 0; nn < NDV; ++nn)
-        vf[nn] = *reinterpret_cast<const u32x4*>(VT + (dv0 + 16 * nn + lr) * RT + 32 * ts + 8 * lg);
+      for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_operand(Vs, RS, 32 * ts, dv0 + 16 * nn + 4 * (lr & 3));
 #pragma unroll
       for (int t = 0; t < NDK; ++t) {
-        const u32x4 kt = *reinterpret_cast<const u32x4*>(KT + state_row(t, lr) * RT + 32 * ts + 8 * lg);
+        // A operand: K^T rows pi(t, m) = columns of the K tile
+        const u32x4 kt = tr_operand(Ks, RS, 32 * ts, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt, vf[nn], Sacc[t][nn]);
       }

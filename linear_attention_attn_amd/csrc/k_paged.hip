@@ -164,6 +164,7 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
   const int g = blockIdx.y;
   const int total = cu_parts[B];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
   const int64_t head_stride = (int64_t)kBlock * D;
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -198,13 +199,21 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
 
     for (int p0 = b_begin; p0 < b_end; p0 += NW * BPW) {
       // ---- issue all loads of this wave's blocks ----
+      // The block ids are wave-uniform: scalar loads, all fetched before any
+      // K/V address is formed, so the K/V loads of the 4 blocks overlap.
+      int32_t blks[BPW];
+#pragma unroll
+      for (int j = 0; j < BPW; ++j) {
+        const int b = p0 + w_s * BPW + j;
+        blks[j] = b < b_end ? btr[b] : -1;
+      }
       u32x4 kf[BPW][KS];
       uint32_t vr[BPW][4][DPL / 2];
       int ntok[BPW];  // valid tokens of each block (0 if absent)
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
-        const int b = p0 + w * BPW + j;
-        int32_t blk = b < b_end ? btr[b] : -1;
+        const int b = p0 + w_s * BPW + j;
+        int32_t blk = blks[j];
         if (blk >= n_blocks) blk = -1;  // defensive: invalid ids are skipped
         ntok[j] = blk >= 0 ? min(kBlock, c - kBlock * b) : 0;
         const int64_t base = ((int64_t)(blk < 0 ? 0 : blk) * H_kv + g) * head_stride;
@@ -528,12 +537,10 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   constexpr int KS = D / 32;    // k steps over the head dim
   constexpr int NDT = D / 16;   // 16-wide head-dim tiles of O^T
   constexpr int KT = 64;        // keys per LDS stage
-  constexpr int KRS = D + 8;    // K tile row stride (elements)
-  constexpr int VRS = KT + 8;   // V^T tile row stride (elements)
+  constexpr int KRS = D + 16;   // K and V tile row stride (elements): 8 mod 32 dwords
   constexpr int CG = D / 8;     // 16-byte column groups of a K/V row
-  constexpr int TGN = 256 / CG; // 4-token groups per staging pass
   __shared__ __align__(16) uint16_t Ks[2][KT * KRS];
-  __shared__ __align__(16) uint16_t Vt[2][D * VRS];
+  __shared__ __align__(16) uint16_t Vs[2][KT * KRS];
 
   const int qtile = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int q0 = cu_q[r], ql = cu_q[r + 1] - q0;
@@ -577,49 +584,52 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     l_run[rt] = 0.f;
   }
 
-  // ---- staging: thread -> (4 tokens, 8 head dims) of the stage ----
-  const int sdg = tid % CG, stg = tid / CG;
-  const bool stager = 4 * stg < KT;
-  u32x4 pk[4], pv[4];
-  auto load_stage = [&](int st) {
+  // ---- staging: wave w stages block w of each 64-key stage (4 blocks) ----
+  // Lane -> (TPL consecutive tokens, one 8-dim column group). The block id is
+  // wave-uniform, so it comes through a scalar load, and it is fetched one
+  // stage ahead of its use.
+  constexpr int TPL = CG / 4;  // tokens per lane: 16 tokens x CG groups / 64 lanes
+  const int scg = l % CG, stk = (l / CG) * TPL;  // column group, first token in the block
+  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
+  auto block_of = [&](int st) -> int32_t {              // raw table entry, validated at use
+    const int key = st * KT + kBlock * w_s;
+    return (st < n_st && key < c) ? btr[key >> 4] : -1;
+  };
+  u32x4 pk[TPL], pv[TPL];
+  auto load_stage = [&](int st, int32_t blk) {
+    if (blk >= n_blocks) blk = -1;  // defensive: invalid ids read as absent
+    const int key0 = st * KT + kBlock * w_s + stk;
+    const int64_t base = ((int64_t)(blk < 0 ? 0 : blk) * H_kv + g) * kBlock * D + 8 * scg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = st * KT + 4 * stg + i;
-      pk[i] = u32x4{0u, 0u, 0u, 0u};
-      pv[i] = pk[i];
-      if (stager && key < c) {
-        const int32_t blk = btr[key >> 4];
-        if (blk >= 0 && blk < n_blocks) {
-          const int64_t off = (((int64_t)blk * H_kv + g) * kBlock + (key & 15)) * D + 8 * sdg;
-          pk[i] = *reinterpret_cast<const u32x4*>(k_pool + off);
-          pv[i] = *reinterpret_cast<const u32x4*>(v_pool + off);
-        }
-      }
+    for (int i = 0; i < TPL; ++i) {
+      const bool ok = blk >= 0 && key0 + i < c;
+      const int64_t off = base + (int64_t)(stk + i) * D;
+      pk[i] = ok ? *reinterpret_cast<const u32x4*>(k_pool + off) : u32x4{0u, 0u, 0u, 0u};
+      pv[i] = ok ? *reinterpret_cast<const u32x4*>(v_pool + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store_stage = [&](int buf) {
-    if (!stager) return;
+    const int row0 = kBlock * w_s + stk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&Ks[buf][(4 * stg + i) * KRS + 8 * sdg]) = pk[i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x2 t;
-      t[0] = ((pv[0][j >> 1] >> (16 * (j & 1))) & 0xffffu) | (((pv[1][j >> 1] >> (16 * (j & 1))) & 0xffffu) << 16);
-      t[1] = ((pv[2][j >> 1] >> (16 * (j & 1))) & 0xffffu) | (((pv[3][j >> 1] >> (16 * (j & 1))) & 0xffffu) << 16);
-      *reinterpret_cast<u32x2*>(&Vt[buf][(8 * sdg + j) * VRS + 4 * stg]) = t;
+    for (int i = 0; i < TPL; ++i) {
+      *reinterpret_cast<u32x4*>(&Ks[buf][(row0 + i) * KRS + 8 * scg]) = pk[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][(row0 + i) * KRS + 8 * scg]) = pv[i];
     }
   };
 
-  load_stage(0);
+  load_stage(0, block_of(0));
   store_stage(0);
+  int32_t blk_next = block_of(1);
+  // retire every load issued so far (Q fragments included) so the stage loop
+  // below only ever waits for its own prefetch
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int st = 0; st < n_st; ++st) {
     const int buf = st & 1;
-    if (st + 1 < n_st) load_stage(st + 1);
+    if (st + 1 < n_st) load_stage(st + 1, blk_next);
     const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vt[buf];
-#pragma nounroll
+    const uint16_t* Vb = Vs[buf];
+#pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int key0 = st * KT + 32 * kk;
       if (key0 >= kend) break;
@@ -697,11 +707,15 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
       // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const u32x4 vf = *reinterpret_cast<const u32x4*>(Vb + (16 * dt + lr) * VRS + 32 * kk + 8 * lg);
+        // V^T rows 16 dt + lr (head dims), keys 32 kk + 8 lg + 0..7: a transposing read
+        const u32x4 vf = tr_operand(Vb, KRS, 32 * kk, 16 * dt + 4 * (lr & 3));
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf, pb[rt], ot[dt][rt]);
       }
     }
+    // the next block id is fetched after the compute: scalar loads share
+    // the LDS counter, so earlier it would delay the first LDS read above
+    blk_next = block_of(st + 2);
     if (st + 1 < n_st) store_stage(buf ^ 1);
     __syncthreads();
   }
