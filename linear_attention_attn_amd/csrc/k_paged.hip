@@ -79,7 +79,7 @@ hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_poo
 // (request, partition) pairs; k_decode_plan lays them out with an exclusive
 // scan, so the attention grid never holds empty workgroups.
 // ============================================================================
-constexpr int kPassBlocks = 16;  // blocks per workgroup pass (4 waves x 4 blocks)
+constexpr int kPassBlocks = 4;  // blocks per workgroup step (4 waves x 1 block)
 constexpr int kMaxParts = 64;
 
 DecodePlan decode_plan(int max_context) {
@@ -138,26 +138,36 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 // Decode, bf16. grid (workers, H_kv), 4 waves; each workgroup walks the
 // (request, partition) items worker, worker + gridDim.x, ... for KV head g.
 //
-// A partition is processed in passes of 16 blocks; in a pass, wave w issues
-// the loads of its 4 blocks (32 KiB of K and V) at once. Scores of the G query
-// heads sharing KV head g come from v_mfma_f32_16x16x32_bf16 (A = the 16 K
-// rows of a block, B = the query heads padded to 16 columns): lane l holds
-// keys 4*(l/16)+i of head l%16. Weights go through LDS to the P.V lanes, which
-// own DPL = D/16 value dims of keys 4*(l/16)+i of each block. Every wave keeps
-// an online softmax; the 4 waves are merged by log-sum-exp at the end.
+// A partition is processed in steps of 8 blocks, 2 per wave, software
+// pipelined: while a wave computes step i from one register buffer, the K/V
+// loads of step i + 1 are in flight into the other. Loads are issued
+// unconditionally (absent blocks read block 0 and are masked), so the
+// compiler's wait counts stay exact. Scores of the G query heads sharing KV
+// head g come from v_mfma_f32_16x16x32_bf16 (A = the 16 K rows of a block,
+// B = the query heads padded to 16 columns): lane l holds keys 4*(l/16)+i of
+// head l%16. The P.V lanes own DPL = D/16 value dims of keys 4*(l/16)+i of
+// each block and fetch the weights they need with shuffles, so the waves
+// never wait for each other inside an item; they are merged by log-sum-exp at
+// the end.
 // ============================================================================
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_paged_decode_bf16(
+struct DecodeBuf {
+  static constexpr int KS = D / 32, DPL = D / 16, BPW = 1;
+  u32x4 kf[BPW][KS];
+  uint32_t vr[BPW][4][DPL / 2];
+  int ntok[BPW];  // valid tokens of each block (0 if absent)
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void k_paged_decode_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx, int B, int H_q, int H_kv, float scale_log2,
     int part_blocks, int max_parts, float* __restrict__ ws, const int32_t* __restrict__ cu_parts) {
-  constexpr int KS = D / 32;    // k steps of the score MFMA
-  constexpr int DPL = D / 16;   // value dims per lane in P.V
+  using Buf = DecodeBuf<D, G>;
+  constexpr int KS = Buf::KS, DPL = Buf::DPL, BPW = Buf::BPW;
   constexpr int NW = 4;
-  constexpr int BPW = 4;        // blocks per wave per pass
-  __shared__ __align__(16) float s_p[NW][G][BPW * kBlock];
-  __shared__ float s_corr[NW][G];
+  constexpr int STEP = NW * BPW;  // blocks per workgroup step
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ __align__(16) float s_acc[NW][G][D];
 
@@ -180,6 +190,7 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
     const int n_parts = n_parts_of(c, max_blocks, part_blocks, max_parts);
     const int b_begin = part * part_blocks;
     const int b_end = min(nblk, b_begin + part_blocks);
+    const int nsteps = (b_end - b_begin + STEP - 1) / STEP;
     const int h0 = g * G;
     const int32_t* btr = bt + (int64_t)r * max_blocks;
 
@@ -188,108 +199,107 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
     for (int s = 0; s < KS; ++s)
       qf[s] = lr < G ? *reinterpret_cast<const u32x4*>(q + ((int64_t)r * H_q + h0 + lr) * D + 32 * s + 8 * lg)
                      : u32x4{0u, 0u, 0u, 0u};
-    float l_part[G], acc[G][DPL];
+    float m_all[G], l_part[G], acc[G][DPL];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
+      m_all[hh] = -INFINITY;
       l_part[hh] = 0.f;
 #pragma unroll
       for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
     }
-    float m_own = -INFINITY;  // running max of head lr (lanes lr < G), scaled domain
 
-    for (int p0 = b_begin; p0 < b_end; p0 += NW * BPW) {
-      // ---- issue all loads of this wave's blocks ----
-      // The block ids are wave-uniform: scalar loads, all fetched before any
-      // K/V address is formed, so the K/V loads of the 4 blocks overlap.
-      int32_t blks[BPW];
+    // ---- loads of one step into a buffer (always issued) ----
+    auto load = [&](Buf& X, int st) {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
-        const int b = p0 + w_s * BPW + j;
-        blks[j] = b < b_end ? btr[b] : -1;
-      }
-      u32x4 kf[BPW][KS];
-      uint32_t vr[BPW][4][DPL / 2];
-      int ntok[BPW];  // valid tokens of each block (0 if absent)
-#pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        const int b = p0 + w_s * BPW + j;
-        int32_t blk = blks[j];
-        if (blk >= n_blocks) blk = -1;  // defensive: invalid ids are skipped
-        ntok[j] = blk >= 0 ? min(kBlock, c - kBlock * b) : 0;
-        const int64_t base = ((int64_t)(blk < 0 ? 0 : blk) * H_kv + g) * head_stride;
+        const int b = b_begin + st * STEP + w_s * BPW + j;
+        int32_t blk = b < b_end ? btr[b] : -1;
+        const bool ok = blk >= 0 && blk < n_blocks;
+        X.ntok[j] = ok ? min(kBlock, c - kBlock * b) : 0;
+        const int64_t base = ((int64_t)(ok ? blk : 0) * H_kv + g) * head_stride;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kf[j][s] = blk >= 0 ? *reinterpret_cast<const u32x4*>(k_pool + base + lr * D + 32 * s + 8 * lg)
-                              : u32x4{0u, 0u, 0u, 0u};
+          X.kf[j][s] = *reinterpret_cast<const u32x4*>(k_pool + base + lr * D + 32 * s + 8 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint16_t* vp = v_pool + base + (4 * lg + i) * D + DPL * lr;
           if constexpr (DPL == 8) {
-            const u32x4 x = blk >= 0 ? *reinterpret_cast<const u32x4*>(vp) : u32x4{0u, 0u, 0u, 0u};
-            vr[j][i][0] = x[0]; vr[j][i][1] = x[1]; vr[j][i][2] = x[2]; vr[j][i][3] = x[3];
+            const u32x4 x = *reinterpret_cast<const u32x4*>(vp);
+            X.vr[j][i][0] = x[0]; X.vr[j][i][1] = x[1]; X.vr[j][i][2] = x[2]; X.vr[j][i][3] = x[3];
           } else {
-            const u32x2 x = blk >= 0 ? *reinterpret_cast<const u32x2*>(vp) : u32x2{0u, 0u};
-            vr[j][i][0] = x[0]; vr[j][i][1] = x[1];
+            const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+            X.vr[j][i][0] = x[0]; X.vr[j][i][1] = x[1];
           }
         }
       }
-      // ---- scores: lane holds key 4*lg + i of block j for head lr ----
+    };
+    // ---- one step: scores, online softmax, P.V ----
+    auto compute = [&](const Buf& X) {
       float x[BPW][4];
       float bm = -INFINITY;
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sc = mfma16x16x32(kf[j][s], qf[s], sc);
+        for (int s = 0; s < KS; ++s) sc = mfma16x16x32(X.kf[j][s], qf[s], sc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[j][i] = (4 * lg + i < ntok[j]) ? sc[i] * scale_log2 : -INFINITY;
+          x[j][i] = (4 * lg + i < X.ntok[j]) ? sc[i] * scale_log2 : -INFINITY;
           bm = fmaxf(bm, x[j][i]);
         }
       }
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_own, bm);
-      const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-      if (lr < G) {
-#pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-          f32x4 pv4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv4[i] = fast_exp2(x[j][i] - mref);
-          *reinterpret_cast<f32x4*>(&s_p[w][lr][j * kBlock + 4 * lg]) = pv4;
-        }
-        if (lg == 0) s_corr[w][lr] = (m_own == -INFINITY) ? 0.f : fast_exp2(m_own - mref);
-      }
-      m_own = m_new;
-      __syncthreads();
-      // ---- P.V: lane owns dims DPL*lr .. +DPL of keys 4*lg + i of each block ----
+      // every lane tracks the running max of all G heads (head hh's block max sits in lane hh)
+      float corr[G];
+      float m_own = 0.f;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float corr = s_corr[w][hh];
-        float ls = l_part[hh] * corr;
+        const float mn = fmaxf(m_all[hh], __shfl(bm, hh));
+        corr[hh] = (m_all[hh] == -INFINITY) ? 0.f : fast_exp2(m_all[hh] - mn);
+        m_all[hh] = mn;
+        if (lr == hh) m_own = (mn == -INFINITY) ? 0.f : mn;
+      }
+      float p[BPW][4];
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr;
+      for (int j = 0; j < BPW; ++j)
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&s_p[w][hh][j * kBlock + 4 * lg]);
+        for (int i = 0; i < 4; ++i) p[j][i] = fast_exp2(x[j][i] - m_own);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float ls = l_part[hh] * corr[hh];
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr[hh];
+#pragma unroll
+        for (int j = 0; j < BPW; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // keys beyond the context have weight 0; their values may be junk
-            const bool ok = 4 * lg + i < ntok[j];
-            const float pw = ok ? p4[i] : 0.f;
+            const bool ok = 4 * lg + i < X.ntok[j];
+            const float pw = ok ? __shfl(p[j][i], 16 * lg + hh) : 0.f;
             ls += pw;
 #pragma unroll
             for (int d2 = 0; d2 < DPL / 2; ++d2) {
-              const uint32_t vv = ok ? vr[j][i][d2] : 0u;
+              const uint32_t vv = ok ? X.vr[j][i][d2] : 0u;
               acc[hh][2 * d2] = __builtin_fmaf(pw, bf16_lo(vv), acc[hh][2 * d2]);
               acc[hh][2 * d2 + 1] = __builtin_fmaf(pw, bf16_hi(vv), acc[hh][2 * d2 + 1]);
             }
           }
-        }
         l_part[hh] = ls;
       }
-      __syncthreads();  // s_p / s_corr are rewritten by the next pass
+    };
+
+    // Two-buffer pipeline with an unconditional body (a step past the end is
+    // fully masked: block 0 is read and every key gets weight 0), which keeps
+    // the compiler's count of loads in flight exact: each compute waits only
+    // for its own buffer while the other buffer's loads stay outstanding.
+    Buf A, Bf;
+    load(A, 0);
+    for (int st = 0; st < nsteps; st += 2) {
+      load(Bf, st + 1);
+      compute(A);
+      load(A, st + 2);
+      compute(Bf);
     }
 
     // ---- combine the 4 token rows of the wave (same running max) ----
@@ -310,10 +320,12 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
 #pragma unroll
         for (int d = 0; d < DPL; ++d) s_acc[w][hh][DPL * lr + d] = acc[hh][d];
     }
-    if (l < G) s_m[w][l] = m_own;
     if (l == 0) {
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) s_l[w][hh] = l_part[hh];
+      for (int hh = 0; hh < G; ++hh) {
+        s_m[w][hh] = m_all[hh];
+        s_l[w][hh] = l_part[hh];
+      }
     }
     __syncthreads();
     const bool single = (n_parts == 1);
@@ -322,19 +334,19 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
       float M = -INFINITY;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][hh]);
-      float L = 0.f, A = 0.f;
+      float L = 0.f, Acc = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
         const float f = (s_m[ww][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[ww][hh] - M);
         L += s_l[ww][hh] * f;
-        A += s_acc[ww][hh][d] * f;
+        Acc += s_acc[ww][hh][d] * f;
       }
       const int head = h0 + hh;
       if (single) {
-        o[((int64_t)r * H_q + head) * D + d] = (uint16_t)f32_to_bf16_bits(L > 0.f ? A / L : 0.f);
+        o[((int64_t)r * H_q + head) * D + d] = (uint16_t)f32_to_bf16_bits(L > 0.f ? Acc / L : 0.f);
       } else {
         float* wp = ws + (((int64_t)r * H_q + head) * max_parts + part) * (D + 2);
-        wp[2 + d] = A;
+        wp[2 + d] = Acc;
         if (d == 0) {
           wp[0] = M;
           wp[1] = L;
