@@ -85,6 +85,12 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int rs, int ro
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + a.lo * b.lo + a.hi * b.hi for bf16 pairs, in fp32 (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         acc, false);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 }  // namespace hy

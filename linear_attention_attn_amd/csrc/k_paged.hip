@@ -20,6 +20,11 @@ namespace hy {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.f;  // log2 headroom before the softmax reference moves
+constexpr float kRescaleSum = 65536.f;     // bound on a lane's p-sum before causal prefill rescales
+constexpr float kMinusHuge = -0x1p100f;    // finite stand-in for -inf as a softmax reference
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 constexpr int kPrefillNR = 2;    // 16-row tiles per wave in causal prefill
 
 // ============================================================================
@@ -589,10 +594,14 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m_run: the row's softmax reference in the scaled (log2) domain, starting
+  // at a finite stand-in for -inf so that p = 2^(s - m) is +inf for any real
+  // score (forcing the first exact pass) and 0 for a masked one (never NaN).
+  // l_run: this lane's share of the row's sum of p.
   float m_run[NR], l_run[NR];
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
-    m_run[rt] = -INFINITY;
+    m_run[rt] = kMinusHuge;
     l_run[rt] = 0.f;
   }
 
@@ -629,6 +638,68 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     }
   };
 
+  // ---- scores S^T for 32 keys (half kk of the stage) x this wave's rows ----
+  // Lane (lr, lg) receives keys 32 kk + 8 lg + 4 u + i of row tile rt.
+  auto scores = [&](const uint16_t* Kb, int kk, f32x4 (&sc)[2][NR]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int krow = 32 * kk + 8 * (lr >> 2) + 4 * u + (lr & 3);
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) sc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(Kb + krow * KRS + 32 * s + 8 * lg);
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) sc[u][rt] = mfma16x16x32(kf, qf[rt][s], sc[u][rt]);
+      }
+    }
+  };
+
+  // ---- online softmax pieces ----
+  // p = 2^(s * scale_log2 - m_run), packed to bf16 pairs (the P^T operand);
+  // returns the lane's sum of the rounded p, the values P V actually uses.
+  auto probs = [&](const f32x4 (&sc)[2][NR], int rt, u32x4& pb) -> float {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[4 * u + i] = fast_exp2(__builtin_fmaf(sc[u][rt][i], scale_log2, -m_run[rt]));
+    float ps = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      pb[p2] = pack_bf16x2(x[2 * p2], x[2 * p2 + 1]);
+      ps = dot2_bf16(pb[p2], kOnesBf16x2, ps);
+    }
+    return ps;
+  };
+  auto mask = [&](int key0, f32x4 (&sc)[2][NR]) {  // keys beyond each row's position
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+      const int pos = base_pos + row_pos[rt];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 8 * lg + 4 * u + i > pos) sc[u][rt][i] = -INFINITY;
+    }
+  };
+  auto lane_max = [&](const f32x4 (&sc)[2][NR], int rt) -> float {
+    return fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
+                 fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
+  };
+
+  // ---- O^T += V^T P^T for one 32-key half ----
+  auto pv_acc = [&](const uint16_t* Vb, int kk, const u32x4 (&pb)[NR]) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      // V^T rows 16 dt + lr (head dims), keys 32 kk + 8 lg + 0..7: a transposing read
+      const u32x4 vf = tr_operand(Vb, KRS, 32 * kk, 16 * dt + 4 * (lr & 3));
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf, pb[rt], ot[dt][rt]);
+    }
+  };
+
   load_stage(0, block_of(0));
   store_stage(0);
   int32_t blk_next = block_of(1);
@@ -636,101 +707,82 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   // below only ever waits for its own prefetch
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  for (int st = 0; st < n_st; ++st) {
+  // One 64-key stage. Both halves' scores are issued first, so the second
+  // half's MFMAs can run under the first half's softmax. A half past the
+  // last key of the workgroup is fully masked (its p are 0).
+  //
+  // Softmax: the common case needs no cross-lane work. p is taken against
+  // the current reference m_run and each lane checks its own sums; only when
+  // some lane's sum exceeds kRescaleSum (a score above the reference by about
+  // log2(kRescaleSum), or the first keys of a row) does the wave take the
+  // exact path: per row, the maximum over the stage's 64 keys across the four
+  // lanes holding it, a new reference, the rescale of the row's partial sums
+  // and accumulators, and p again. One such point per stage keeps a single
+  // join in the loop body.
+  auto stage = [&](auto diag, int st) {
     const int buf = st & 1;
     if (st + 1 < n_st) load_stage(st + 1, blk_next);
     const uint16_t* Kb = Ks[buf];
     const uint16_t* Vb = Vs[buf];
+    f32x4 sa[2][NR], sb[2][NR];
+    u32x4 pa[NR], pb2[NR];
+    float psa[NR], psb[NR];
+    scores(Kb, 0, sa);
+    scores(Kb, 1, sb);
+    if constexpr (decltype(diag)::value) {
+      mask(st * KT, sa);
+      mask(st * KT + 32, sb);
+    }
+    bool over = false;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int key0 = st * KT + 32 * kk;
-      if (key0 >= kend) break;
-      // ---- scores S^T for 32 keys x this wave's 64 rows ----
-      f32x4 sc[2][NR];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int krow = 32 * kk + 8 * (lr >> 2) + 4 * u + (lr & 3);
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) sc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(Kb + krow * KRS + 32 * s + 8 * lg);
-#pragma unroll
-          for (int rt = 0; rt < NR; ++rt) sc[u][rt] = mfma16x16x32(kf, qf[rt][s], sc[u][rt]);
-        }
-      }
-      // ---- online softmax per row; lane holds keys key0 + 8 lg + 4u + i ----
-      // Scores stay unscaled until the exponent: p = 2^(s * scale_log2 - m),
-      // m in the scaled domain. The reference m moves only when a row's new
-      // maximum exceeds it by more than kRescale (then p <= 2^kRescale), so
-      // the accumulator rescale is rare and done under a wave-uniform branch.
-      const bool diag = key0 + 31 > pos_lo;  // some key may lie beyond some row
-      u32x4 pb[NR];
+    for (int rt = 0; rt < NR; ++rt) {
+      psa[rt] = probs(sa, rt, pa[rt]);
+      psb[rt] = probs(sb, rt, pb2[rt]);
+      over |= !(psa[rt] + psb[rt] <= kRescaleSum);  // also catches +inf
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
       float corr[NR];
-      bool any_rescale = false;
 #pragma unroll
       for (int rt = 0; rt < NR; ++rt) {
-        const int pos = base_pos + row_pos[rt];
-        if (diag) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (key0 + 8 * lg + 4 * u + i > pos) sc[u][rt][i] = -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
-                         fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
+        float mx = fmaxf(lane_max(sa, rt), lane_max(sb, rt));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float ms = mx * scale_log2;
+        const float ms = mx * scale_log2;  // -inf when every key of the stage is masked
         corr[rt] = 1.f;
-        if (ms > m_run[rt] + kRescale) {
-          corr[rt] = fast_exp2(m_run[rt] - ms);  // 0 when m_run is -inf
+        if (ms > m_run[rt]) {
+          corr[rt] = fast_exp2(m_run[rt] - ms);  // 0 on the row's first real key
           l_run[rt] *= corr[rt];
           m_run[rt] = ms;
-          any_rescale = true;
         }
-        float x[8];
-        float ps = 0.f;
-        const float mref = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];  // row with no key yet
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(__builtin_fmaf(sc[u][rt][i], scale_log2, -mref));
-            x[4 * u + i] = e;
-            ps += e;
-          }
-        l_run[rt] += ps;
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) pb[rt][p2] = pack_bf16x2(x[2 * p2], x[2 * p2 + 1]);
+        psa[rt] = probs(sa, rt, pa[rt]);
+        psb[rt] = probs(sb, rt, pb2[rt]);
       }
-      if (__builtin_amdgcn_ballot_w64(any_rescale)) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int rt = 0; rt < NR; ++rt) {
-            ot[dt][rt][0] *= corr[rt];
-            ot[dt][rt][1] *= corr[rt];
-            ot[dt][rt][2] *= corr[rt];
-            ot[dt][rt][3] *= corr[rt];
-          }
-      }
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        // V^T rows 16 dt + lr (head dims), keys 32 kk + 8 lg + 0..7: a transposing read
-        const u32x4 vf = tr_operand(Vb, KRS, 32 * kk, 16 * dt + 4 * (lr & 3));
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf, pb[rt], ot[dt][rt]);
-      }
+        for (int rt = 0; rt < NR; ++rt) {
+          ot[dt][rt][0] *= corr[rt];
+          ot[dt][rt][1] *= corr[rt];
+          ot[dt][rt][2] *= corr[rt];
+          ot[dt][rt][3] *= corr[rt];
+        }
     }
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) l_run[rt] += psa[rt] + psb[rt];
+    pv_acc(Vb, 0, pa);
+    pv_acc(Vb, 1, pb2);
     // the next block id is fetched after the compute: scalar loads share
     // the LDS counter, so earlier it would delay the first LDS read above
     blk_next = block_of(st + 2);
     if (st + 1 < n_st) store_stage(buf ^ 1);
     __syncthreads();
-  }
+  };
+  // stages whose 64 keys all lie at or before the workgroup's first query
+  // position need no causal mask
+  const int n_plain = min(n_st, (pos_lo + 1) / KT);
+  int st = 0;
+  for (; st < n_plain; ++st) stage(BoolTag<false>{}, st);
+  for (; st < n_st; ++st) stage(BoolTag<true>{}, st);
 
   // ---- normalise and store: lane holds O^T[d = 16 dt + 4 lg + i][row lr] ----
 #pragma unroll
