@@ -527,19 +527,21 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 }
 
 // ============================================================================
-// Causal prefill, bf16 (MFMA, FlashAttention-style). grid (query tiles, H_kv,
-// B), 4 waves. A workgroup takes QT = 64 NR / G query positions of one request
-// for all G query heads sharing KV head g (64 NR rows), so every K/V tile
-// staged in LDS serves G heads. Wave w owns 16 NR rows (NR tiles of 16).
+// Causal prefill, bf16 (MFMA, FlashAttention-style). 1-D grid over (query
+// tile, H_kv, B), 4 waves. A workgroup takes QT = 64 NR / G query positions
+// of one request for all G query heads sharing KV head g (64 NR rows), so
+// every K/V tile staged in LDS serves G heads. Wave w owns 16 NR rows (NR
+// tiles of 16).
 //
-// Per 64-key stage (4 blocks gathered through the block table, K row-major
-// and V transposed in LDS, double-buffered with the next stage's global loads
-// in flight) and per 32-key half:
+// Per 64-key stage (4 blocks gathered through the block table, K and V
+// row-major in LDS, double-buffered with the next stage's global loads in
+// flight) and per 32-key half:
 //   S^T = K Q^T   (two 16-key tiles; the key order inside each tile is
 //                  permuted so that a lane ends up with 8 consecutive keys of
 //                  its row, i.e. directly the B operand below)
-//   online softmax over the lane's row (max via two cross-row shuffles)
-//   O^T += V^T P^T (A = V^T fragment from LDS, B = P^T from registers)
+//   online softmax over the lane's row (see the stage body)
+//   O^T += V^T P^T (A = V^T fragment via transposing LDS reads, B = P^T
+//                  from registers)
 // Computing O^T rather than O keeps the softmax row, the score column and the
 // output column on the same lane, so rescaling needs no data movement.
 // ============================================================================
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
-    int H_kv, float scale_log2) {
+    int H_kv, float scale_log2, int n_qt, int n_req) {
   constexpr int ROWS = 64 * NR; // rows (query position, head) per workgroup: 4 waves x 16 NR
   constexpr int QT = ROWS / G;  // query positions per workgroup
   constexpr int KS = D / 32;    // k steps over the head dim
@@ -559,7 +561,13 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   __shared__ __align__(16) uint16_t Ks[2][KT * KRS];
   __shared__ __align__(16) uint16_t Vs[2][KT * KRS];
 
-  const int qtile = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  // 1-D grid, heaviest query tiles first (longest causal spans start early
+  // and short ones fill the tail); consecutive ids walk over (g, r), so the
+  // tiles of one (request, KV head) sit gridDim.x / n_qt ids apart, a
+  // multiple of 8 whenever H_kv * B is, and land on the same XCD and L2.
+  const int n_gr = H_kv * n_req;
+  const int qtile = n_qt - 1 - (int)blockIdx.x / n_gr;
+  const int g = (int)blockIdx.x % n_gr % H_kv, r = (int)blockIdx.x % n_gr / H_kv;
   const int q0 = cu_q[r], ql = cu_q[r + 1] - q0;
   const int i0 = qtile * QT;
   if (i0 >= ql) return;
@@ -815,10 +823,11 @@ hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, cons
 #define HY_PP(DD, GG)                                                                          \
   do {                                                                                         \
     constexpr int QT_ = 64 * kPrefillNR / GG;                                                  \
-    dim3 grid((unsigned)((max_q_len + QT_ - 1) / QT_), (unsigned)H_kv, (unsigned)B);           \
+    const int n_qt = (max_q_len + QT_ - 1) / QT_;                                              \
+    dim3 grid((unsigned)(n_qt * H_kv * B));                                                    \
     hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR>), grid, dim3(256), 0, s, (const uint16_t*)q, \
                        (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
-                       bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2);                             \
+                       bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                    \
   } while (0)
 #define HY_PP_G(DD)                   \
   switch (G) {                        \
