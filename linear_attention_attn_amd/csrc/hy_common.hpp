@@ -93,4 +93,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// compile-time integer as a type, and a loop over 0..N-1 unrolled at compile
+// time (the body receives IntTag<i>)
+template <int V> struct IntTag { static constexpr int value = V; };
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(IntTag<I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
 }  // namespace hy

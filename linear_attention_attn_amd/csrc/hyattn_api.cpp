@@ -146,7 +146,7 @@ bool prefill_chunk_ok(int D, int chunk, hyattn_dtype dt) {
   if (dt == HYATTN_F32) return chunk >= 1 && chunk <= hy::kMaxChunkF32;
   if (chunk < 16 || chunk > 256 || chunk % 16 != 0) return false;
   const int Cp = (chunk + 31) & ~31;
-  const size_t lds = (size_t)2 * Cp * (D + 16) * 2;  // K and V tiles of the bf16 kernel
+  const size_t lds = (size_t)(2 * Cp + 64) * D * 2;  // K, V tiles and the Q pair ring of the bf16 kernel
   return lds <= 160 * 1024;
 }
 

@@ -200,26 +200,30 @@ __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ 
 //
 // One workgroup (4 waves) per (request, head). Wave w owns the value columns
 // [w*D/4, (w+1)*D/4) of the state, kept in fp32 accumulator registers for the
-// whole request. Per chunk, K and V are staged row-major in LDS (72 KiB at
-// C = 128, so two workgroups share a CU and hide each other's staging); Q
-// fragments come straight from global memory. Each wave computes, for its
-// value columns:
-//   O_c   = Q_c S  (S split into bf16 hi + lo, two MFMAs: fp32-faithful)
-//         + tril(Q_c K_c^T) V_c  (scores in fp32, split hi + lo likewise)
-//   S    += K_c^T V_c (accumulated straight into the fp32 state registers)
-// Token-contiguous operands (K^T rows, V columns) are read from the
-// row-major tiles with the transposing LDS read. Index permutations keep the
-// other operands contiguous 16-byte reads:
+// whole request. Per chunk, K and V are staged in LDS (64 KiB at C = 128, so
+// two workgroups share a CU and hide each other's staging), and the query
+// rows are taken two 16-row tiles at a time (both see the same key blocks,
+// so each K or V fragment read from LDS serves two tiles). For its value
+// columns each wave computes
+//   O_c^T = S^T Q_c^T   (S split into bf16 hi + lo: two MFMAs, fp32-faithful)
+//         + V_c^T tril(Q_c K_c^T)^T   (scores in fp32, split hi + lo likewise)
+//   S    += K_c^T V_c   (accumulated straight into the fp32 state registers)
+// O^T rather than O puts four consecutive value columns of one query row in
+// a lane, so outputs leave as 8-byte stores. Token-contiguous operands (V
+// columns, K^T rows) come from row-major tiles through the transposing LDS
+// read. Index permutations keep the other operands contiguous reads:
 //  * state rows: accumulator tile t, row m holds key dim
 //      pi(t, m) = 32*(t/2) + 8*(m/4) + 4*(t%2) + m%4
 //    so that tiles 2s and 2s+1 together give each lane the 8 consecutive key
 //    dims 32s + 8*(l/16) + 0..7 that its Q fragment holds;
 //  * score tiles: P^T = K Q^T over 32 keys as two 16-row tiles whose row m
 //    is key 8*(m/4) + 4u + m%4 (u = tile), so each lane ends up with the 8
-//    consecutive keys 8*(l/16) + 0..7 of one query row, i.e. directly the A
-//    operand of P V.
-// LDS rows are D + 16 elements long (a stride of 8 mod 32 dwords), which
-// spreads both the row reads and the transposing reads over all banks.
+//    consecutive keys 8*(l/16) + 0..7 of one query row, i.e. directly the B
+//    operand of V^T P^T.
+// LDS rows hold D elements with their 16-byte chunks XOR-swizzled per row,
+// chosen so that each access pattern (Q and K fragment reads over 16 rows,
+// transposing reads over 4-8 rows, 16-byte staging writes) spreads over all
+// banks.
 // ============================================================================
 template <int D>
 struct PrefillCfg {
@@ -228,11 +232,46 @@ struct PrefillCfg {
   static constexpr int NDV = DVW / 16; // 16-wide value tiles per wave
   static constexpr int NDK = D / 16;   // 16-row key-dim tiles of the state
   static constexpr int KS = D / 32;    // 32-wide k steps over the head dim
-  static constexpr int RS = D + 16;    // LDS row stride (elements)
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
 };
 
 __device__ __forceinline__ int state_row(int t, int m) {
   return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3);
+}
+
+// chunk XORs of the staged tiles (rows relative to the tile)
+template <int D>
+__device__ __forceinline__ int qswz(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return ((row >> 3) & 3) | ((row & 3) << 2);
+  else return ((row >> 3) & 3) | (((row >> 1) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 1) | (row & 8);
+  else return (row & 2) | (((row >> 3) & 1) << 2);
+}
+// element offset of (row, col) in a tile with chunk XOR x
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col, int x) {
+  return row * D + 8 * ((col >> 3) ^ x) + (col & 7);
+}
+// 8 consecutive rows 8*(l/16) + 0..7 of column c(l%16 / 4) + l%4 of a
+// swizzled 32-row tile as an MFMA operand (two transposing reads). The
+// source lane (l/16, l%16) addresses row 8*(l/16) + (l%16)/4 (and + 4),
+// column col_src; the row's XOR is the same for + 4 (it ignores bit 2).
+template <int D, bool IS_K>
+__device__ __forceinline__ u32x4 tr_swz(const uint16_t* tile, int col_src) {
+  const int l = threadIdx.x & 63;
+  const int row = 8 * (l >> 4) + ((l & 15) >> 2);
+  const uint16_t* p = tile + swz_off<D>(row, col_src, IS_K ? kswz<D>(row) : vswz<D>(row));
+  const u32x2 a = ds_read_tr16(p);
+  const u32x2 b = ds_read_tr16(p + 4 * D);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
@@ -247,9 +286,8 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 
 template <int D>
 size_t prefill_bf16_lds_bytes(int C) {
-  using Cfg = PrefillCfg<D>;
   const int Cp = (C + 31) & ~31;
-  return (size_t)2 * Cp * Cfg::RS * 2;
+  return (size_t)(2 * Cp + 2 * 32) * D * 2;  // K and V tiles of the chunk + Q pair ring
 }
 
 template <int D>
@@ -258,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int C) {
   using Cfg = PrefillCfg<D>;
-  constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, RS = Cfg::RS;
+  constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = Cfg::CPR;
   extern __shared__ __align__(16) uint16_t lds_h[];
 
   const int unit = blockIdx.x;
@@ -269,7 +307,8 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
 
   const int Cp = (C + 31) & ~31;
   uint16_t* Ks = lds_h;
-  uint16_t* Vs = Ks + Cp * RS;
+  uint16_t* Vs = Ks + Cp * D;
+  uint16_t* Qr = Vs + Cp * D;  // [2][32][D]: Q rows of the current and the next pair
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int dv0 = w * Cfg::DVW;
@@ -289,14 +328,43 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
       for (int i = 0; i < 4; ++i)
         Sacc[t][n][i] = S[(int64_t)state_row(t, 4 * lg + i) * D + dv0 + 16 * n + lr];
 
+  // ---- Q pairs (32 query rows) stream through a 2-deep LDS ring ----
+  // Pair p of the request (chunk c0 = C * (p / pairs per chunk)) sits in
+  // slot p % 2. Its rows are fetched by the whole workgroup one pair ahead
+  // (two 16-byte loads per thread) and stored after the current pair's
+  // compute, behind the barrier that closes it.
+  constexpr int QPT = 32 * CPR / 256;  // 16-byte pieces per thread per pair
+  const int qc = tid % CPR, qr0 = tid / CPR;
+  u32x4 qst[QPT];
+  const int ppc = (C + 31) >> 5;  // pairs per full chunk
+  auto fetch_pair = [&](int cc0, int jj) {  // rows 32 jj .. of the chunk at cc0 (zero past T)
+    const int nn_ = (T - cc0 < C) ? (T - cc0) : C;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int a = 32 * jj + qr0 + (256 / CPR) * i;
+      qst[i] = (cc0 < T && a < nn_) ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(cc0 + a) * ldx + 8 * qc)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_pair = [&](int slot) {
+    uint16_t* dst = Qr + slot * 32 * D;
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int a = qr0 + (256 / CPR) * i;
+      *reinterpret_cast<u32x4*>(dst + swz_off<D>(a, 8 * qc, qswz<D>(a))) = qst[i];
+    }
+  };
+  int pslot = 0;  // ring slot of the current pair
+  fetch_pair(0, 0);
+  store_pair(0);  // made visible by the first staging barrier below
+
   for (int c0 = 0; c0 < T; c0 += C) {
     const int n = (T - c0 < C) ? (T - c0) : C;
     __syncthreads();  // the previous chunk's tiles are no longer read
-    // ---- stage K and V row-major (rows past n are zero) ----
+    // ---- stage K and V (rows past n are zero) ----
     {
-      constexpr int CG = D / 8;         // 16-byte column groups per row
-      constexpr int TGS = 256 / CG;     // 4-token groups per pass
-      const int dk8 = tid % CG, tg = tid / CG;
+      constexpr int TGS = 256 / CPR;    // 4-token groups per pass
+      const int dk8 = tid % CPR, tg = tid / CPR;
       for (int slab = 0; slab < Cp; slab += 4 * TGS) {
         const int a0 = slab + 4 * tg;
         if (a0 >= Cp) continue;
@@ -315,42 +383,47 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(Ks + (a0 + i) * RS + 8 * dk8) = rk[i];
-          *reinterpret_cast<u32x4*>(Vs + (a0 + i) * RS + 8 * dk8) = rv[i];
+          const int a = a0 + i;
+          *reinterpret_cast<u32x4*>(Ks + swz_off<D>(a, 8 * dk8, kswz<D>(a))) = rk[i];
+          *reinterpret_cast<u32x4*>(Vs + swz_off<D>(a, 8 * dk8, vswz<D>(a))) = rv[i];
         }
       }
     }
     __syncthreads();
 
-    // ---- outputs, 16 query rows at a time ----
-    // The state registers are not updated before the last row tile, so the
-    // bf16 hi/lo B operands of Q S (the state before this chunk) are rebuilt
-    // from them per row tile instead of being kept live.
-    const int nrt = (n + 15) >> 4;
-    // Q fragments come from global memory one row tile ahead of their use
-    u32x4 qnext[KS];
+    // ---- outputs, two 16-row tiles (32 query rows) at a time ----
+    // Both tiles of a pair see the same key blocks, so every K and V
+    // fragment read from LDS feeds two tiles, and the pair gives 4 to 8
+    // independent accumulator chains. The pair's Q fragments arrive one pair
+    // ahead of their use.
+    const int npr = (n + 31) >> 5;
+    for (int j = 0; j < npr; ++j) {
+      // the next pair: this chunk's j + 1, or the next chunk's first
+      if (j + 1 < npr) fetch_pair(c0, j + 1);
+      else fetch_pair(c0 + C, 0);
+      u32x4 qf[2][KS];
+      {
+        const uint16_t* src = Qr + pslot * 32 * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qnext[s] = lr < n ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(c0 + lr) * ldx + 32 * s + 8 * lg)
-                        : u32x4{0u, 0u, 0u, 0u};
-    for (int rt = 0; rt < nrt; ++rt) {
-      const int row = 16 * rt + lr;
-      u32x4 qf[KS];
+        for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = qnext[s];
-      if (rt + 1 < nrt) {
-        const int nrow = row + 16;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          qnext[s] = nrow < n ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(c0 + nrow) * ldx + 32 * s + 8 * lg)
-                              : u32x4{0u, 0u, 0u, 0u};
+          for (int s = 0; s < KS; ++s) {
+            const int row = 16 * t2 + lr;
+            qf[t2][s] = *reinterpret_cast<const u32x4*>(src + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
+          }
       }
-      f32x4 Oacc[NDV];
+
+      f32x4 Ot[2][NDV];
 #pragma unroll
-      for (int nn = 0; nn < NDV; ++nn) {
-        Oacc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      // inter-chunk: O^T += S^T Q^T with the state before this chunk
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int nn = 0; nn < NDV; ++nn) {
           float x[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -359,60 +432,90 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
           }
           u32x4 shi, slo;
           split8(x, shi, slo);
-          Oacc[nn] = mfma16x16x32(qf[s], shi, Oacc[nn]);
-          Oacc[nn] = mfma16x16x32(qf[s], slo, Oacc[nn]);
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            Ot[t2][nn] = mfma16x16x32(shi, qf[t2][s], Ot[t2][nn]);
+            Ot[t2][nn] = mfma16x16x32(slo, qf[t2][s], Ot[t2][nn]);
+          }
         }
       }
-      const int nkb = (16 * rt + 15) / 32 + 1;
-      for (int kb32 = 0; kb32 < nkb; ++kb32) {
-        f32x4 pt[2];
+
+      // intra-chunk: O^T += V^T P^T, P = tril(Q K^T), keys 0 .. 32 j + 31
+      for (int kb32 = 0; kb32 <= j; ++kb32) {
+        const uint16_t* Kt = Ks + 32 * kb32 * D;
+        const uint16_t* Vt = Vs + 32 * kb32 * D;
+        f32x4 pt[2][2];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) pt[t2][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          pt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int krow = 32 * kb32 + 8 * (lr >> 2) + 4 * u + (lr & 3);
+          const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + krow * RS + 32 * s + 8 * lg);
-            pt[u] = mfma16x16x32(kf, qf[s], pt[u]);
+            const u32x4 kf =
+                *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 32 * s + 8 * lg, kswz<D>(krow)));
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) pt[t2][u] = mfma16x16x32(kf, qf[t2][s], pt[t2][u]);
           }
         }
-        float pv[8];
+        u32x4 phi[2], plo[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int row = 32 * j + 16 * t2 + lr;
+          float pv[8];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = 32 * kb32 + 8 * lg + 4 * u + i;
-            pv[4 * u + i] = (key <= row) ? pt[u][i] : 0.f;
-          }
-        u32x4 phi, plo;
-        split8(pv, phi, plo);
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = 32 * kb32 + 8 * lg + 4 * u + i;
+              pv[4 * u + i] = (key <= row) ? pt[t2][u][i] : 0.f;
+            }
+          split8(pv, phi[t2], plo[t2]);
+        }
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) {
-          const u32x4 vf = tr_operand(Vs, RS, 32 * kb32, dv0 + 16 * nn + 4 * (lr & 3));
-          Oacc[nn] = mfma16x16x32(phi, vf, Oacc[nn]);
-          Oacc[nn] = mfma16x16x32(plo, vf, Oacc[nn]);
+          const u32x4 vf = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            Ot[t2][nn] = mfma16x16x32(vf, phi[t2], Ot[t2][nn]);
+            Ot[t2][nn] = mfma16x16x32(vf, plo[t2], Ot[t2][nn]);
+          }
         }
       }
+
+      // lane holds O^T[value col 16 nn + 4 lg + i][query row lr] of each tile
 #pragma unroll
-      for (int nn = 0; nn < NDV; ++nn)
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int row = 32 * j + 16 * t2 + lr;
+        if (row < n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int orow = 16 * rt + 4 * lg + i;
-          if (orow < n)
-            ob[(int64_t)(c0 + orow) * ldx + dv0 + 16 * nn + lr] = (uint16_t)f32_to_bf16_bits(Oacc[nn][i]);
+          for (int nn = 0; nn < NDV; ++nn) {
+            u32x2 t4;
+            t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
+            t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
+            *reinterpret_cast<u32x2*>(ob + (int64_t)(c0 + row) * ldx + dv0 + 16 * nn + 4 * lg) = t4;
+          }
         }
+      }
+      pslot ^= 1;
+      store_pair(pslot);  // its previous readers finished before the last barrier
+      __syncthreads();
     }
 
     // ---- state update: S += K_c^T V_c ----
     const int nts = (n + 31) >> 5;
     for (int ts = 0; ts < nts; ++ts) {
+      const uint16_t* Kt = Ks + 32 * ts * D;
+      const uint16_t* Vt = Vs + 32 * ts * D;
       u32x4 vf[NDV];
 #pragma unroll
-      for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_operand(Vs, RS, 32 * ts, dv0 + 16 * nn + 4 * (lr & 3));
+      for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
 #pragma unroll
       for (int t = 0; t < NDK; ++t) {
         // A operand: K^T rows pi(t, m) = columns of the K tile
-        const u32x4 kt = tr_operand(Ks, RS, 32 * ts, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
+        const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt, vf[nn], Sacc[t][nn]);
       }
@@ -442,19 +545,20 @@ hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q
   dim3 grid((unsigned)(n_req * H)), block(256);
   hipError_t e;
   if (bf16) {
+#define HY_LP(DD)                                                                              \
+  do {                                                                                         \
+    const size_t lds = prefill_bf16_lds_bytes<DD>(chunk);                                      \
+    if ((e = allow_lds(k_linear_prefill_bf16<DD>, lds)) != hipSuccess) return e;               \
+    hipLaunchKernelGGL((k_linear_prefill_bf16<DD>), grid, block, lds, s, layer_states, n_slots, \
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, \
+                       cu, slots, H, chunk);                                                   \
+  } while (0)
     if (D == 128) {
-      const size_t lds = prefill_bf16_lds_bytes<128>(chunk);
-      if ((e = allow_lds(k_linear_prefill_bf16<128>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_linear_prefill_bf16<128>, grid, block, lds, s, layer_states, n_slots,
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                         (uint16_t*)o, cu, slots, H, chunk);
+      HY_LP(128);
     } else {
-      const size_t lds = prefill_bf16_lds_bytes<64>(chunk);
-      if ((e = allow_lds(k_linear_prefill_bf16<64>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_linear_prefill_bf16<64>, grid, block, lds, s, layer_states, n_slots,
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                         (uint16_t*)o, cu, slots, H, chunk);
+      HY_LP(64);
     }
+#undef HY_LP
   } else {
     const size_t lds = (size_t)(D * D + chunk * chunk) * sizeof(float);
     if (D == 128) {
