@@ -202,6 +202,52 @@ def component_times(wl, reps=3):
     return out
 
 
+PMC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                           "paged_decode_hbm_traffic.md")
+DECODE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_attn_amd",
+                             "csrc", "k_paged.hip")
+
+
+def measured_traffic():
+    """HBM bytes per paged-decode launch from the committed counter summary.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch of
+    k_paged_decode_bf16 on this workload), the factors that map each counter
+    onto bytes (from a plain copy of known size) and the SHA-256 of the
+    kernel source the counters were taken with. Returns None when the file is
+    missing or the source has changed since.
+    """
+    import hashlib
+    import re
+    try:
+        text = open(PMC_SUMMARY).read()
+        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
+    try:
+        if fields["kernel_source_sha256"] != src:
+            return None
+        kib = (float(fields["fetch_kib_per_dispatch"]) * float(fields["fetch_scale"])
+               + float(fields["write_kib_per_dispatch"]) * float(fields["write_scale"]))
+    except (KeyError, ValueError):
+        return None
+    return int(kib * 1024)
+
+
+def copy_probe(reps=3):
+    """A plain 2 GiB device copy (the calibration target of the HBM counters)."""
+    import torch
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "reps": reps}), flush=True)
+
+
 def dominant_kernel_roofline(wl, steps):
     """Average paged-decode launch time over all full layers of `steps` steps."""
     import torch
@@ -225,9 +271,9 @@ def dominant_kernel_roofline(wl, steps):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ts]))
     nbytes = wl.decode_kv_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(kernel="paged_decode (k_paged_decode_bf16 + k_paged_merge)", bound="hbm",
-                achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+    return dict(kernel="paged_decode (k_decode_plan + k_paged_decode_bf16 + k_paged_merge)",
+                bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                 algorithmic_bytes_per_launch=nbytes, avg_launch_ms=round(ms, 4))
 
 
@@ -316,6 +362,8 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--ctx-scale", type=float, default=1.0,
                     help="scale of the longest decode context (1.0 = 131072)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 2 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -323,6 +371,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe()
+        return
     from linear_attention_attn_amd import hyattn as hy
     hy.load()
     props = torch.cuda.get_device_properties(0)
@@ -370,6 +421,8 @@ def main():
     log(f"dominant kernel: {roof}")
     out["roofline"] = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     out["roofline"]["kernel"] = roof["kernel"]
+    out["roofline"]["algorithmic_bytes_per_launch"] = roof["algorithmic_bytes_per_launch"]
+    out["roofline"]["avg_launch_ms"] = roof["avg_launch_ms"]
     if not args.no_components:
         comp = component_times(wl)
         n_lin, n_full = wl.n_lin, wl.n_full
