@@ -72,6 +72,30 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// The same transposing read as an opaque instruction: the compiler neither
+// tracks it nor waits for it, so the caller must wait (lds_wait_all) before
+// using the result. For loops that keep global-to-LDS loads in flight, which
+// the compiler would otherwise drain before every transposing read.
+__device__ __forceinline__ u32x2 ds_read_tr16_raw(const uint16_t* lds) {
+  const uint32_t a = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)lds));
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+// Wait until every outstanding LDS operation of the wave has completed; the
+// registers passed in are tied to the wait so no use of them moves above it.
+template <int N>
+__device__ __forceinline__ void lds_wait_all(u32x4 (&x)[N]) {
+  static_assert(N == 8 || N == 4, "lds_wait_all: 4 or 8 fragments");
+  if constexpr (N == 8)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                   "+v"(x[6]), "+v"(x[7]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+}
+
 // 8 consecutive rows row0 + 8*(l/16) + 0..7 of column col_q(l%16 / 4) + l%4 of
 // a row-major bf16 tile (row stride rs elements) as a 16x16x32 MFMA operand:
 // two transposing reads; col_q is the lane's column base for its l%16 / 4.

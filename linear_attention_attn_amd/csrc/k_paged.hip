@@ -533,9 +533,13 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 // every K/V tile staged in LDS serves G heads. Wave w owns 16 NR rows (NR
 // tiles of 16).
 //
-// Per 64-key stage (4 blocks gathered through the block table, K and V
-// row-major in LDS, double-buffered with the next stage's global loads in
-// flight) and per 32-key half:
+// K and V reach LDS through direct global-to-LDS loads (global_load_lds:
+// no registers hold the data in flight) in 32-key stages (two 16-token
+// blocks), kept in a ring of 4 stage buffers: stage st + 3 is requested
+// while stage st is used, so three stages of loads are in flight behind the
+// computation. Each lane's 16-byte load is aimed so that the tiles land
+// XOR-swizzled per row (the K score reads and the V transposing reads are
+// free of bank conflicts). Per stage:
 //   S^T = K Q^T   (two 16-key tiles; the key order inside each tile is
 //                  permuted so that a lane ends up with 8 consecutive keys of
 //                  its row, i.e. directly the B operand below)
@@ -545,6 +549,17 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 // Computing O^T rather than O keeps the softmax row, the score column and the
 // output column on the same lane, so rescaling needs no data movement.
 // ============================================================================
+template <int D>
+__device__ __forceinline__ int pf_kswz(int row) {  // chunk XOR of a K row of a stage
+  if constexpr (D == 128) return (row & 3) | ((row >> 1) & 12);
+  else return ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+template <int D>
+__device__ __forceinline__ int pf_vswz(int row) {  // chunk XOR of a V row of a stage (even)
+  if constexpr (D == 128) return ((row & 3) << 1) | (row & 8);
+  else return (row & 2) | (((row >> 3) & 1) << 2);
+}
+
 template <int D, int G, int NR>
 __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
@@ -555,11 +570,13 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   constexpr int QT = ROWS / G;  // query positions per workgroup
   constexpr int KS = D / 32;    // k steps over the head dim
   constexpr int NDT = D / 16;   // 16-wide head-dim tiles of O^T
-  constexpr int KT = 64;        // keys per LDS stage
-  constexpr int KRS = D + 16;   // K and V tile row stride (elements): 8 mod 32 dwords
-  constexpr int CG = D / 8;     // 16-byte column groups of a K/V row
-  __shared__ __align__(16) uint16_t Ks[2][KT * KRS];
-  __shared__ __align__(16) uint16_t Vs[2][KT * KRS];
+  constexpr int KT = 32;        // keys per stage
+  constexpr int NB = 4;         // stage buffers in the ring
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // rows covered by one wave-wide 16-byte load
+  constexpr int IPB = 16 / RPI; // such loads per 16-token block
+  __shared__ __align__(16) uint16_t Ks[NB][KT * D];
+  __shared__ __align__(16) uint16_t Vs[NB][KT * D];
 
   // 1-D grid, heaviest query tiles first (longest causal spans start early
   // and short ones fill the tail); consecutive ids walk over (g, r), so the
@@ -573,7 +590,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   if (i0 >= ql) return;
   const int c = min(ctx[r], max_blocks * kBlock);
   const int base_pos = c - ql;  // position of this request's first query
-  if (base_pos < 0) return;     // more queries than context: invalid input
+  if (base_pos < 0 || n_blocks <= 0) return;  // more queries than context: invalid input
   const int kend = min(c, base_pos + i0 + QT);
   const int n_st = (kend + KT - 1) / KT;
   const int pos_lo = base_pos + i0;  // smallest query position of the workgroup
@@ -613,50 +630,57 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     l_run[rt] = 0.f;
   }
 
-  // ---- staging: wave w stages block w of each 64-key stage (4 blocks) ----
-  // Lane -> (TPL consecutive tokens, one 8-dim column group). The block id is
-  // wave-uniform, so it comes through a scalar load, and it is fetched one
-  // stage ahead of its use.
-  constexpr int TPL = CG / 4;  // tokens per lane: 16 tokens x CG groups / 64 lanes
-  const int scg = l % CG, stk = (l / CG) * TPL;  // column group, first token in the block
-  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
-  auto block_of = [&](int st) -> int32_t {              // raw table entry, validated at use
-    const int key = st * KT + kBlock * w_s;
+  // ---- staging: wave w moves tensor (w & 1: K, V) of block (w >> 1) of
+  // each stage, IPB wave-wide 16-byte loads straight into LDS. The block id
+  // is wave-uniform (a scalar load, fetched one stage ahead of its use).
+  // Lane l of load i fills row 16 b + RPI i + l / CPR, chunk position
+  // l % CPR, so it fetches the logical chunk that the row's XOR maps there.
+  const int w_s = __builtin_amdgcn_readfirstlane(w);
+  const int sb = w_s >> 1;          // block of the stage this wave moves
+  const bool sv = (w_s & 1) != 0;   // V (else K)
+  const uint16_t* pool = sv ? v_pool : k_pool;
+  auto block_of = [&](int st) -> int32_t {  // raw table entry, validated at use
+    const int key = st * KT + kBlock * sb;
     return (st < n_st && key < c) ? btr[key >> 4] : -1;
   };
-  u32x4 pk[TPL], pv[TPL];
-  auto load_stage = [&](int st, int32_t blk) {
-    if (blk >= n_blocks) blk = -1;  // defensive: invalid ids read as absent
-    const int key0 = st * KT + kBlock * w_s + stk;
-    const int64_t base = ((int64_t)(blk < 0 ? 0 : blk) * H_kv + g) * kBlock * D + 8 * scg;
+  auto issue_stage = [&](int st, int32_t blk) {
+    if (blk < 0 || blk >= n_blocks) blk = 0;  // absent: any valid block, zeroed after landing
+    const uint16_t* src = pool + ((int64_t)blk * H_kv + g) * kBlock * D;
+    uint16_t* dst = (sv ? Vs[st % NB] : Ks[st % NB]) + kBlock * sb * D;
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      const bool ok = blk >= 0 && key0 + i < c;
-      const int64_t off = base + (int64_t)(stk + i) * D;
-      pk[i] = ok ? *reinterpret_cast<const u32x4*>(k_pool + off) : u32x4{0u, 0u, 0u, 0u};
-      pv[i] = ok ? *reinterpret_cast<const u32x4*>(v_pool + off) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < IPB; ++i) {
+      const int tok = RPI * i + l / CPR;         // token within the block
+      const int row = kBlock * sb + tok;         // row within the stage
+      const int x = sv ? pf_vswz<D>(row) : pf_kswz<D>(row);
+      __builtin_amdgcn_global_load_lds(src + tok * D + 8 * ((l % CPR) ^ x),
+                                       (__attribute__((address_space(3))) void*)(dst + RPI * i * D),
+                                       16, 0, 0);
     }
   };
-  auto store_stage = [&](int buf) {
-    const int row0 = kBlock * w_s + stk;
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      *reinterpret_cast<u32x4*>(&Ks[buf][(row0 + i) * KRS + 8 * scg]) = pk[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][(row0 + i) * KRS + 8 * scg]) = pv[i];
-    }
+  // rows of a landed stage that hold no valid key (past the context, or an
+  // absent block) are cleared by the wave that moved them: V must be finite
+  // there, as masked keys still meet it in P V with weight 0
+  auto clear_invalid = [&](int st, int32_t blk) {
+    const int key0 = st * KT + kBlock * sb;
+    const int nvalid = (blk < 0 || blk >= n_blocks) ? 0 : min(kBlock, max(0, c - key0));
+    if (nvalid == kBlock) return;
+    uint16_t* dst = (sv ? Vs[st % NB] : Ks[st % NB]) + kBlock * sb * D;
+    for (int e = l; e < kBlock * CPR; e += 64)
+      if (e / CPR >= nvalid) *reinterpret_cast<u32x4*>(dst + 8 * e) = u32x4{0u, 0u, 0u, 0u};
   };
 
-  // ---- scores S^T for 32 keys (half kk of the stage) x this wave's rows ----
-  // Lane (lr, lg) receives keys 32 kk + 8 lg + 4 u + i of row tile rt.
-  auto scores = [&](const uint16_t* Kb, int kk, f32x4 (&sc)[2][NR]) {
+  // ---- scores S^T for the stage's 32 keys x this wave's rows ----
+  // Lane (lr, lg) receives keys 8 lg + 4 u + i of row tile rt.
+  auto scores = [&](const uint16_t* Kb, f32x4 (&sc)[2][NR]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int krow = 32 * kk + 8 * (lr >> 2) + 4 * u + (lr & 3);
+      const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
 #pragma unroll
       for (int rt = 0; rt < NR; ++rt) sc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(Kb + krow * KRS + 32 * s + 8 * lg);
+        const u32x4 kf =
+            *reinterpret_cast<const u32x4*>(Kb + krow * D + 8 * ((4 * s + lg) ^ pf_kswz<D>(krow)));
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) sc[u][rt] = mfma16x16x32(kf, qf[rt][s], sc[u][rt]);
       }
@@ -697,62 +721,57 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
                  fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
   };
 
-  // ---- O^T += V^T P^T for one 32-key half ----
-  auto pv_acc = [&](const uint16_t* Vb, int kk, const u32x4 (&pb)[NR]) {
+  // ---- O^T += V^T P^T for the stage ----
+  // V^T rows 16 dt + lr (head dims), keys 8 lg + 0..7: two transposing reads
+  // per tile; source lane (lg, lr) addresses key row 8 lg + lr / 4 (+ 4),
+  // head dims 16 dt + 4 (lr % 4) + 0..3 (rows + 4 share the row's XOR). The
+  // reads are issued as plain instructions with one explicit wait: the
+  // compiler would otherwise drain every global-to-LDS load in flight before
+  // a transposing read, which would serialise the stage ring.
+  auto pv_acc = [&](const uint16_t* Vb, const u32x4 (&pb)[NR]) {
+    const int vrow = 8 * lg + (lr >> 2);
+    u32x4 vf[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      // V^T rows 16 dt + lr (head dims), keys 32 kk + 8 lg + 0..7: a transposing read
-      const u32x4 vf = tr_operand(Vb, KRS, 32 * kk, 16 * dt + 4 * (lr & 3));
-#pragma unroll
-      for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf, pb[rt], ot[dt][rt]);
+      const int vcol = 16 * dt + 4 * (lr & 3);
+      const uint16_t* vp = Vb + vrow * D + 8 * ((vcol >> 3) ^ pf_vswz<D>(vrow)) + (vcol & 7);
+      const u32x2 v0 = ds_read_tr16_raw(vp);
+      const u32x2 v1 = ds_read_tr16_raw(vp + 4 * D);
+      vf[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
     }
+    lds_wait_all(vf);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf[dt], pb[rt], ot[dt][rt]);
   };
 
-  load_stage(0, block_of(0));
-  store_stage(0);
-  int32_t blk_next = block_of(1);
-  // retire every load issued so far (Q fragments included) so the stage loop
-  // below only ever waits for its own prefetch
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  // One 64-key stage. Both halves' scores are issued first, so the second
-  // half's MFMAs can run under the first half's softmax. A half past the
-  // last key of the workgroup is fully masked (its p are 0).
-  //
-  // Softmax: the common case needs no cross-lane work. p is taken against
-  // the current reference m_run and each lane checks its own sums; only when
-  // some lane's sum exceeds kRescaleSum (a score above the reference by about
-  // log2(kRescaleSum), or the first keys of a row) does the wave take the
-  // exact path: per row, the maximum over the stage's 64 keys across the four
-  // lanes holding it, a new reference, the rescale of the row's partial sums
-  // and accumulators, and p again. One such point per stage keeps a single
-  // join in the loop body.
-  auto stage = [&](auto diag, int st) {
-    const int buf = st & 1;
-    if (st + 1 < n_st) load_stage(st + 1, blk_next);
-    const uint16_t* Kb = Ks[buf];
-    const uint16_t* Vb = Vs[buf];
-    f32x4 sa[2][NR], sb[2][NR];
-    u32x4 pa[NR], pb2[NR];
-    float psa[NR], psb[NR];
-    scores(Kb, 0, sa);
-    scores(Kb, 1, sb);
-    if constexpr (decltype(diag)::value) {
-      mask(st * KT, sa);
-      mask(st * KT + 32, sb);
-    }
+  // One 32-key stage. Softmax: the common case needs no cross-lane work. p is
+  // taken against the current reference m_run and each lane checks its own
+  // sum; only when some lane's sum exceeds kRescaleSum (a score above the
+  // reference by about log2(kRescaleSum), or the first keys of a row) does
+  // the wave take the exact path: per row, the maximum over the stage's keys
+  // across the four lanes holding it, a new reference, the rescale of the
+  // row's partial sums and accumulators, and p again.
+  auto compute = [&](auto diag, int st) {
+    const uint16_t* Kb = Ks[st % NB];
+    const uint16_t* Vb = Vs[st % NB];
+    f32x4 sc[2][NR];
+    u32x4 pb[NR];
+    float ps[NR];
+    scores(Kb, sc);
+    if constexpr (decltype(diag)::value) mask(st * KT, sc);
     bool over = false;
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) {
-      psa[rt] = probs(sa, rt, pa[rt]);
-      psb[rt] = probs(sb, rt, pb2[rt]);
-      over |= !(psa[rt] + psb[rt] <= kRescaleSum);  // also catches +inf
+      ps[rt] = probs(sc, rt, pb[rt]);
+      over |= !(ps[rt] <= kRescaleSum);  // also catches +inf
     }
     if (__builtin_amdgcn_ballot_w64(over)) {
       float corr[NR];
 #pragma unroll
       for (int rt = 0; rt < NR; ++rt) {
-        float mx = fmaxf(lane_max(sa, rt), lane_max(sb, rt));
+        float mx = lane_max(sc, rt);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float ms = mx * scale_log2;  // -inf when every key of the stage is masked
@@ -762,8 +781,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
           l_run[rt] *= corr[rt];
           m_run[rt] = ms;
         }
-        psa[rt] = probs(sa, rt, pa[rt]);
-        psb[rt] = probs(sb, rt, pb2[rt]);
+        ps[rt] = probs(sc, rt, pb[rt]);
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -776,16 +794,47 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
         }
     }
 #pragma unroll
-    for (int rt = 0; rt < NR; ++rt) l_run[rt] += psa[rt] + psb[rt];
-    pv_acc(Vb, 0, pa);
-    pv_acc(Vb, 1, pb2);
-    // the next block id is fetched after the compute: scalar loads share
-    // the LDS counter, so earlier it would delay the first LDS read above
-    blk_next = block_of(st + 2);
-    if (st + 1 < n_st) store_stage(buf ^ 1);
-    __syncthreads();
+    for (int rt = 0; rt < NR; ++rt) l_run[rt] += ps[rt];
+    pv_acc(Vb, pb);
   };
-  // stages whose 64 keys all lie at or before the workgroup's first query
+
+  // ---- the stage ring ----
+  // Each wave issues IPB loads per stage, and stages complete in order, so
+  // waiting for stage st leaves the IPB loads of each later stage already
+  // requested outstanding. Stage st + 3 goes into the buffer of stage st - 1,
+  // which every wave finished reading before the barrier of stage st.
+  int32_t blk_ring[NB];  // block ids of the stages in flight (wave-uniform)
+  // the Q fragments land first, so no later wait for them can drain the ring
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) {
+    blk_ring[i] = block_of(i);
+    if (i < n_st) issue_stage(i, blk_ring[i]);
+  }
+  blk_ring[NB - 1] = block_of(NB - 1);
+  auto stage = [&](auto diag, int st) {
+    const int ahead = n_st - 1 - st;  // stages requested after this one: min(ahead, NB - 2)
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPB));  // vmcnt(2 IPB)
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | IPB);   // vmcnt(IPB)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+    const int32_t blk = blk_ring[0];
+    if (st * KT + KT > c || blk < 0 || blk >= n_blocks) clear_invalid(st, blk);
+    // workgroup barrier without the release fence of __syncthreads, which
+    // would also drain the global-to-LDS loads still in flight: the stage's
+    // own loads were waited for above and LDS writes are waited for here
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (st + NB - 1 < n_st) issue_stage(st + NB - 1, blk_ring[NB - 1]);
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) blk_ring[i] = blk_ring[i + 1];
+    compute(diag, st);
+    // the block id after next is fetched after the compute: scalar loads
+    // share the LDS counter, so earlier it would delay the LDS reads above
+    blk_ring[NB - 1] = block_of(st + NB);
+  };
+  // stages whose keys all lie at or before the workgroup's first query
   // position need no causal mask
   const int n_plain = min(n_st, (pos_lo + 1) / KT);
   int st = 0;
