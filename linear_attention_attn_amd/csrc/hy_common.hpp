@@ -87,13 +87,15 @@ __device__ __forceinline__ u32x2 ds_read_tr16_raw(const uint16_t* lds) {
 // registers passed in are tied to the wait so no use of them moves above it.
 template <int N>
 __device__ __forceinline__ void lds_wait_all(u32x4 (&x)[N]) {
-  static_assert(N == 8 || N == 4, "lds_wait_all: 4 or 8 fragments");
+  static_assert(N == 8 || N == 4 || N == 2, "lds_wait_all: 2, 4 or 8 fragments");
   if constexpr (N == 8)
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
                    "+v"(x[6]), "+v"(x[7]));
-  else
+  else if constexpr (N == 4)
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]));
 }
 
 // 8 consecutive rows row0 + 8*(l/16) + 0..7 of column col_q(l%16 / 4) + l%4 of
@@ -116,6 +118,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima): vmcnt is split over
+// bits 3:0 and 15:14.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // compile-time integer as a type, and a loop over 0..N-1 unrolled at compile
 // time (the body receives IntTag<i>)

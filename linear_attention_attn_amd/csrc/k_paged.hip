@@ -142,37 +142,49 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 // ============================================================================
 // Decode, bf16. grid (workers, H_kv), 4 waves; each workgroup walks the
 // (request, partition) items worker, worker + gridDim.x, ... for KV head g.
+// Wave w of a workgroup takes blocks w, w + 4, ... of the partition.
 //
-// A partition is processed in steps of 8 blocks, 2 per wave, software
-// pipelined: while a wave computes step i from one register buffer, the K/V
-// loads of step i + 1 are in flight into the other. Loads are issued
-// unconditionally (absent blocks read block 0 and are masked), so the
-// compiler's wait counts stay exact. Scores of the G query heads sharing KV
-// head g come from v_mfma_f32_16x16x32_bf16 (A = the 16 K rows of a block,
-// B = the query heads padded to 16 columns): lane l holds keys 4*(l/16)+i of
-// head l%16. The P.V lanes own DPL = D/16 value dims of keys 4*(l/16)+i of
-// each block and fetch the weights they need with shuffles, so the waves
-// never wait for each other inside an item; they are merged by log-sum-exp at
-// the end.
+// K and V blocks reach LDS through direct global-to-LDS loads (no registers
+// hold data in flight), each wave keeping its own ring of 4 block slots:
+// block j + 3 is requested while block j is used, so three blocks (24 KiB
+// at D = 128) per wave are in flight behind the computation and the waves
+// never synchronise inside an item. One workgroup fills a CU's LDS, which
+// is what bounds the bytes in flight.
+//   scores: v_mfma_f32_16x16x32_bf16 with A = the 16 K rows of the block
+//           (each lane's K fragment lands at its own LDS offset), B = the G
+//           query heads padded to 16 columns; lane l holds keys 4*(l/16)+i
+//           of head l%16, which is directly the B operand of P V below;
+//   softmax: a lazy reference per head, as in causal prefill (the common
+//           case needs no cross-lane work);
+//   P V:    O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, the V^T operand by
+//           transposing reads of the row-major, chunk-swizzled V tile.
+// The waves are merged by log-sum-exp at the end of the item.
 // ============================================================================
-template <int D, int G>
-struct DecodeBuf {
-  static constexpr int KS = D / 32, DPL = D / 16, BPW = 1;
-  u32x4 kf[BPW][KS];
-  uint32_t vr[BPW][4][DPL / 2];
-  int ntok[BPW];  // valid tokens of each block (0 if absent)
-};
+constexpr int kDecodeRing = 4;  // block slots per wave
+
+template <int D>
+constexpr size_t decode_lds_bytes() {
+  return (size_t)4 * kDecodeRing * 2 * kBlock * D * sizeof(uint16_t);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void k_paged_decode_bf16(
+__global__ __launch_bounds__(256) void k_paged_decode_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx, int B, int H_q, int H_kv, float scale_log2,
     int part_blocks, int max_parts, float* __restrict__ ws, const int32_t* __restrict__ cu_parts) {
-  using Buf = DecodeBuf<D, G>;
-  constexpr int KS = Buf::KS, DPL = Buf::DPL, BPW = Buf::BPW;
+  constexpr int KS = D / 32;     // k steps of the scores
+  constexpr int NDT = D / 16;    // 16-dim tiles of O^T
   constexpr int NW = 4;
-  constexpr int STEP = NW * BPW;  // blocks per workgroup step
+  constexpr int NB = kDecodeRing;
+  constexpr int CPT = D / 8;     // 16-byte chunks per token row
+  constexpr int RPI = 64 / CPT;  // V rows per wave-wide 16-byte load
+  constexpr int NVI = kBlock / RPI;
+  constexpr int IPB = KS + NVI;  // loads per block
+  constexpr int SLOT = 2 * kBlock * D;  // elements per slot: K then V
+  extern __shared__ __align__(16) uint16_t dec_lds[];
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ __align__(16) float s_acc[NW][G][D];
 
@@ -180,7 +192,10 @@ __global__ __launch_bounds__(256, 2) void k_paged_decode_bf16(
   const int total = cu_parts[B];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
-  const int64_t head_stride = (int64_t)kBlock * D;
+  uint16_t* ring = dec_lds + w_s * NB * SLOT;
+  // even chunk XOR of V row t of a block (transposing reads of 8 rows x 2
+  // chunks per 32 lanes hit distinct banks)
+  auto vswz = [](int t) -> int { return D == 128 ? 2 * (t & 7) : 2 * ((t >> 1) & 3); };
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     int lo = 0, hi = B;  // cu_parts[lo] <= item < cu_parts[hi]
@@ -195,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void k_paged_decode_bf16(
     const int n_parts = n_parts_of(c, max_blocks, part_blocks, max_parts);
     const int b_begin = part * part_blocks;
     const int b_end = min(nblk, b_begin + part_blocks);
-    const int nsteps = (b_end - b_begin + STEP - 1) / STEP;
+    const int nbw = max(0, (b_end - b_begin - w_s + NW - 1) / NW);  // this wave's blocks
     const int h0 = g * G;
     const int32_t* btr = bt + (int64_t)r * max_blocks;
 
@@ -204,132 +219,153 @@ __global__ __launch_bounds__(256, 2) void k_paged_decode_bf16(
     for (int s = 0; s < KS; ++s)
       qf[s] = lr < G ? *reinterpret_cast<const u32x4*>(q + ((int64_t)r * H_q + h0 + lr) * D + 32 * s + 8 * lg)
                      : u32x4{0u, 0u, 0u, 0u};
-    float m_all[G], l_part[G], acc[G][DPL];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      m_all[hh] = -INFINITY;
-      l_part[hh] = 0.f;
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[hh][d] = 0.f;
-    }
+    // the Q fragments land first, so no later wait for them drains the ring
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // ---- loads of one step into a buffer (always issued) ----
-    auto load = [&](Buf& X, int st) {
+    f32x4 ot[NDT];
 #pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        const int b = b_begin + st * STEP + w_s * BPW + j;
-        int32_t blk = b < b_end ? btr[b] : -1;
-        const bool ok = blk >= 0 && blk < n_blocks;
-        X.ntok[j] = ok ? min(kBlock, c - kBlock * b) : 0;
-        const int64_t base = ((int64_t)(ok ? blk : 0) * H_kv + g) * head_stride;
+    for (int dt = 0; dt < NDT; ++dt) ot[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kMinusHuge, l_run = 0.f;  // head lr's reference and this lane's share of its sum
+
+    // ---- block j of this wave: global block b = b_begin + w + 4 j ----
+    auto table = [&](int j) -> int32_t {  // raw table entry, validated at use
+      return j < nbw ? btr[b_begin + w_s + NW * j] : -1;
+    };
+    auto issue = [&](int j, int32_t blk) {
+      if (blk < 0 || blk >= n_blocks) blk = 0;  // absent: any valid block, masked and cleared
+      const uint16_t* kb = k_pool + ((int64_t)blk * H_kv + g) * kBlock * D;
+      const uint16_t* vb = v_pool + ((int64_t)blk * H_kv + g) * kBlock * D;
+      uint16_t* slot = ring + (j % NB) * SLOT;
+      // K: load s puts lane l's score operand (key l % 16, dims 32 s + 8 (l / 16) + 0..7)
+      // at its own 16 bytes of a 1 KiB piece
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          X.kf[j][s] = *reinterpret_cast<const u32x4*>(k_pool + base + lr * D + 32 * s + 8 * lg);
+      for (int s = 0; s < KS; ++s)
+        __builtin_amdgcn_global_load_lds(kb + lr * D + 32 * s + 8 * lg,
+                                         (__attribute__((address_space(3))) void*)(slot + s * 512),
+                                         16, 0, 0);
+      // V: row-major, chunk c of row t at position c ^ vswz(t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint16_t* vp = v_pool + base + (4 * lg + i) * D + DPL * lr;
-          if constexpr (DPL == 8) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(vp);
-            X.vr[j][i][0] = x[0]; X.vr[j][i][1] = x[1]; X.vr[j][i][2] = x[2]; X.vr[j][i][3] = x[3];
-          } else {
-            const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
-            X.vr[j][i][0] = x[0]; X.vr[j][i][1] = x[1];
-          }
-        }
+      for (int i = 0; i < NVI; ++i) {
+        const int t = RPI * i + l / CPT;
+        const int x = vswz(t);  // (a call inside the builtin's arguments would break the host stub)
+        __builtin_amdgcn_global_load_lds(vb + t * D + 8 * ((l % CPT) ^ x),
+                                         (__attribute__((address_space(3))) void*)(slot + kBlock * D + i * 512),
+                                         16, 0, 0);
       }
     };
-    // ---- one step: scores, online softmax, P.V ----
-    auto compute = [&](const Buf& X) {
-      float x[BPW][4];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < BPW; ++j) {
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) sc = mfma16x16x32(X.kf[j][s], qf[s], sc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[j][i] = (4 * lg + i < X.ntok[j]) ? sc[i] * scale_log2 : -INFINITY;
-          bm = fmaxf(bm, x[j][i]);
-        }
-      }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      // every lane tracks the running max of all G heads (head hh's block max sits in lane hh)
-      float corr[G];
-      float m_own = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float mn = fmaxf(m_all[hh], __shfl(bm, hh));
-        corr[hh] = (m_all[hh] == -INFINITY) ? 0.f : fast_exp2(m_all[hh] - mn);
-        m_all[hh] = mn;
-        if (lr == hh) m_own = (mn == -INFINITY) ? 0.f : mn;
-      }
-      float p[BPW][4];
-#pragma unroll
-      for (int j = 0; j < BPW; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[j][i] = fast_exp2(x[j][i] - m_own);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float ls = l_part[hh] * corr[hh];
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[hh][d] *= corr[hh];
-#pragma unroll
-        for (int j = 0; j < BPW; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // keys beyond the context have weight 0; their values may be junk
-            const bool ok = 4 * lg + i < X.ntok[j];
-            const float pw = ok ? __shfl(p[j][i], 16 * lg + hh) : 0.f;
-            ls += pw;
-#pragma unroll
-            for (int d2 = 0; d2 < DPL / 2; ++d2) {
-              const uint32_t vv = ok ? X.vr[j][i][d2] : 0u;
-              acc[hh][2 * d2] = __builtin_fmaf(pw, bf16_lo(vv), acc[hh][2 * d2]);
-              acc[hh][2 * d2 + 1] = __builtin_fmaf(pw, bf16_hi(vv), acc[hh][2 * d2 + 1]);
-            }
-          }
-        l_part[hh] = ls;
-      }
+    auto ntok_of = [&](int j, int32_t blk) -> int {  // valid keys of block j
+      if (blk < 0 || blk >= n_blocks) return 0;
+      return min(kBlock, c - kBlock * (b_begin + w_s + NW * j));
     };
 
-    // Two-buffer pipeline with an unconditional body (a step past the end is
-    // fully masked: block 0 is read and every key gets weight 0), which keeps
-    // the compiler's count of loads in flight exact: each compute waits only
-    // for its own buffer while the other buffer's loads stay outstanding.
-    Buf A, Bf;
-    load(A, 0);
-    for (int st = 0; st < nsteps; st += 2) {
-      load(Bf, st + 1);
-      compute(A);
-      load(A, st + 2);
-      compute(Bf);
+    int32_t blk_ring[NB];
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) {
+      blk_ring[i] = table(i);
+      if (i < nbw) issue(i, blk_ring[i]);
+    }
+    blk_ring[NB - 1] = table(NB - 1);
+
+    for (int j = 0; j < nbw; ++j) {
+      const int ahead = nbw - 1 - j;  // blocks requested after this one: min(ahead, NB - 2)
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPB));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPB));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      const int32_t blk = blk_ring[0];
+      const int ntok = ntok_of(j, blk);
+      const uint16_t* kslot = ring + (j % NB) * SLOT;
+      uint16_t* vslot = ring + (j % NB) * SLOT + kBlock * D;
+      if (ntok < kBlock) {  // rows without a key meet P V with weight 0: make them finite
+        for (int e = l; e < kBlock * CPT; e += 64)
+          if (e / CPT >= ntok) *reinterpret_cast<u32x4*>(vslot + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (j + NB - 1 < nbw) issue(j + NB - 1, blk_ring[NB - 1]);
+#pragma unroll
+      for (int i = 0; i < NB - 1; ++i) blk_ring[i] = blk_ring[i + 1];
+      blk_ring[NB - 1] = table(j + NB);
+
+      // ---- scores ----
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kslot + s * 512 + 8 * l);
+        sc = mfma16x16x32(kf, qf[s], sc);
+      }
+      // ---- softmax over head lr's 4 keys in this lane ----
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (lr < G && 4 * lg + i < ntok) ? sc[i] : -INFINITY;
+      auto probs = [&](uint32_t& p01, uint32_t& p23) -> float {
+        const float e0 = fast_exp2(__builtin_fmaf(x[0], scale_log2, -m_run));
+        const float e1 = fast_exp2(__builtin_fmaf(x[1], scale_log2, -m_run));
+        const float e2 = fast_exp2(__builtin_fmaf(x[2], scale_log2, -m_run));
+        const float e3 = fast_exp2(__builtin_fmaf(x[3], scale_log2, -m_run));
+        p01 = pack_bf16x2(e0, e1);
+        p23 = pack_bf16x2(e2, e3);
+        return dot2_bf16(p23, kOnesBf16x2, dot2_bf16(p01, kOnesBf16x2, 0.f));
+      };
+      uint32_t p01, p23;
+      float ps = probs(p01, p23);
+      if (__builtin_amdgcn_ballot_w64(!(ps <= kRescaleSum))) {
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * scale_log2;  // -inf when the head has no key in the block
+        float corr = 1.f;
+        if (ms > m_run) {
+          corr = fast_exp2(m_run - ms);  // 0 on the head's first key
+          l_run *= corr;
+          m_run = ms;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          ot[dt][0] *= corr;
+          ot[dt][1] *= corr;
+          ot[dt][2] *= corr;
+          ot[dt][3] *= corr;
+        }
+        ps = probs(p01, p23);
+      }
+      l_run += ps;
+      // ---- O^T += V^T P^T ----
+      const u32x2 pb = {p01, p23};
+      u32x4 vv[NDT / 2];
+      {
+        // source lane (lg, lr) addresses key row 4 lg + lr / 4, dims 16 dt + 4 (lr % 4) + 0..3
+        const int t = 4 * lg + (lr >> 2);
+#pragma unroll
+        for (int d2 = 0; d2 < NDT / 2; ++d2) {
+          u32x2 vr[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int col = 16 * (2 * d2 + e) + 4 * (lr & 3);
+            vr[e] = ds_read_tr16_raw(vslot + t * D + 8 * ((col >> 3) ^ vswz(t)) + (col & 7));
+          }
+          vv[d2] = u32x4{vr[0][0], vr[0][1], vr[1][0], vr[1][1]};
+        }
+      }
+      lds_wait_all(vv);
+#pragma unroll
+      for (int d2 = 0; d2 < NDT / 2; ++d2)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const u32x2 va = {vv[d2][2 * e], vv[d2][2 * e + 1]};
+          ot[2 * d2 + e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(s16x4, va), __builtin_bit_cast(s16x4, pb), ot[2 * d2 + e], 0, 0, 0);
+        }
     }
 
-    // ---- combine the 4 token rows of the wave (same running max) ----
+    // ---- combine the 4 key rows of the wave (same reference per head) ----
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    // ---- combine the 4 waves: lane (lr < G, lg) holds dims 16 dt + 4 lg + i of head lr ----
+    if (lr < G) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      l_part[hh] += __shfl_xor(l_part[hh], 16);
-      l_part[hh] += __shfl_xor(l_part[hh], 32);
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) {
-        acc[hh][d] += __shfl_xor(acc[hh][d], 16);
-        acc[hh][d] += __shfl_xor(acc[hh][d], 32);
-      }
-    }
-    // ---- combine the 4 waves ----
-    if (l < 16) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) s_acc[w][hh][DPL * lr + d] = acc[hh][d];
-    }
-    if (l == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        s_m[w][hh] = m_all[hh];
-        s_l[w][hh] = l_part[hh];
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(&s_acc[w][lr][16 * dt + 4 * lg]) = ot[dt];
+      if (lg == 0) {
+        s_m[w][lr] = l_run > 0.f ? m_run : -INFINITY;
+        s_l[w][lr] = l_run;
       }
     }
     __syncthreads();
@@ -499,10 +535,20 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   const unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
   dim3 grid(workers, (unsigned)H_kv), block(256);
 #define HY_PD(DD, GG)                                                                         \
-  hipLaunchKernelGGL((k_paged_decode_bf16<DD, GG>), grid, block, 0, s, (const uint16_t*)q,    \
-                     (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
-                     bt, max_blocks, ctx, B, H_q, H_kv, sl2, plan.part_blocks, plan.max_parts, \
-                     ws, cu_parts)
+  do {                                                                                        \
+    constexpr size_t lds = decode_lds_bytes<DD>();                                            \
+    static bool lds_set = false; /* the attribute is per device function; set once */         \
+    if (!lds_set) {                                                                           \
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_paged_decode_bf16<DD, GG>),    \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
+      if (e != hipSuccess) return e;                                                          \
+      lds_set = true;                                                                         \
+    }                                                                                         \
+    hipLaunchKernelGGL((k_paged_decode_bf16<DD, GG>), grid, block, lds, s, (const uint16_t*)q, \
+                       (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
+                       bt, max_blocks, ctx, B, H_q, H_kv, sl2, plan.part_blocks, plan.max_parts, \
+                       ws, cu_parts);                                                         \
+  } while (0)
 #define HY_PD_G(DD)                   \
   switch (G) {                        \
     case 1: HY_PD(DD, 1); break;      \
@@ -550,12 +596,12 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
 // output column on the same lane, so rescaling needs no data movement.
 // ============================================================================
 template <int D>
-__device__ __forceinline__ int pf_kswz(int row) {  // chunk XOR of a K row of a stage
+__host__ __device__ __forceinline__ int pf_kswz(int row) {  // chunk XOR of a K row of a stage
   if constexpr (D == 128) return (row & 3) | ((row >> 1) & 12);
   else return ((row >> 1) & 1) | ((row >> 2) & 6);
 }
 template <int D>
-__device__ __forceinline__ int pf_vswz(int row) {  // chunk XOR of a V row of a stage (even)
+__host__ __device__ __forceinline__ int pf_vswz(int row) {  // chunk XOR of a V row of a stage (even)
   if constexpr (D == 128) return ((row & 3) << 1) | (row & 8);
   else return (row & 2) | (((row >> 3) & 1) << 2);
 }
@@ -814,9 +860,9 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   blk_ring[NB - 1] = block_of(NB - 1);
   auto stage = [&](auto diag, int st) {
     const int ahead = n_st - 1 - st;  // stages requested after this one: min(ahead, NB - 2)
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * IPB));  // vmcnt(2 IPB)
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | IPB);   // vmcnt(IPB)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPB));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPB));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const int32_t blk = blk_ring[0];
     if (st * KT + KT > c || blk < 0 || blk >= n_blocks) clear_invalid(st, blk);
     // workgroup barrier without the release fence of __syncthreads, which
