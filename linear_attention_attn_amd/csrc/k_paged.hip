@@ -140,8 +140,9 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 }
 
 // ============================================================================
-// Decode, bf16. grid (workers, H_kv), 4 waves; each workgroup walks the
-// (request, partition) items worker, worker + gridDim.x, ... for KV head g.
+// Decode, bf16. 1-D grid over (worker, KV head g), head fastest, 4 waves;
+// each workgroup walks the (request, partition) items worker, worker +
+// n_workers, ... for its KV head.
 // Wave w of a workgroup takes blocks w, w + 4, ... of the partition.
 //
 // K and V blocks reach LDS through direct global-to-LDS loads (no registers
@@ -188,7 +189,10 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ __align__(16) float s_acc[NW][G][D];
 
-  const int g = blockIdx.y;
+  // 1-D grid, KV head fastest: the H_kv workgroups of an item run side by
+  // side and read each block's heads, which are adjacent in the pool
+  const int g = (int)blockIdx.x % H_kv;
+  const int worker = (int)blockIdx.x / H_kv, n_workers = (int)gridDim.x / H_kv;
   const int total = cu_parts[B];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
   // chunks per 32 lanes hit distinct banks)
   auto vswz = [](int t) -> int { return D == 128 ? 2 * (t & 7) : 2 * ((t >> 1) & 3); };
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (int item = worker; item < total; item += n_workers) {
     int lo = 0, hi = B;  // cu_parts[lo] <= item < cu_parts[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -533,7 +537,7 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   // enough workers to fill the chip a few times over; each walks items with stride gridDim.x
   const long bound = (long)B * plan.max_parts;
   const unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
-  dim3 grid(workers, (unsigned)H_kv), block(256);
+  dim3 grid(workers * (unsigned)H_kv), block(256);
 #define HY_PD(DD, GG)                                                                         \
   do {                                                                                        \
     constexpr size_t lds = decode_lds_bytes<DD>();                                            \
