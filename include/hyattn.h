@@ -41,6 +41,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Tokens per block of the paged KV cache (P2 §2.1: fixed 16-token pages). */
+#define HYATTN_BLOCK_TOKENS 16
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -236,6 +239,35 @@ size_t hyattn_hybrid_workspace_bytes(const hyattn_batch* batch);
 hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
                                  const hyattn_layer_io* layers, const hyattn_batch* batch,
                                  hyattn_state_pool* pool, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Memory estimate (page "推理框架适配Hybrid Model：KV Cache管理与算子调度实战",
+ * §3.3 on sizing the two state kinds, §2.1 on what each layer type keeps):
+ * device bytes a set of requests needs, for admission before any allocation.
+ * Full layers keep K and V of every cached token (2 * L_full * H_kv * D *
+ * elem_bytes per token); linear layers keep one H x D x D state per request
+ * (L_lin * H * D * D * elem_bytes), whatever its length. Host only, no GPU.
+ */
+typedef struct {
+  uint64_t kv_bytes;        /* 2 * L_full * H_kv * D * kv_elem_bytes * sum_r ctx_r      */
+  uint64_t kv_paged_bytes;  /* the same with each context rounded up to 16-token blocks */
+  uint64_t kv_blocks;       /* blocks one full layer's pool needs: sum_r ceil(ctx_r/16) */
+  uint64_t state_bytes;     /* L_lin * H * D * D * n_requests * state_elem_bytes        */
+  int n_full_layers;        /* layers of each type in layer_types                       */
+  int n_linear_layers;
+} hyattn_memory_estimate;
+
+/* layer_types: host int32[n_layers] (HYATTN_LAYER_LINEAR / _FULL, anything
+ * else is HYATTN_ERR_UNSUPPORTED_LAYER); context_lens: host int32[n_requests]
+ * (tokens cached per request, >= 0); kv_elem_bytes / state_elem_bytes: bytes
+ * per stored element (2 for bf16, 4 for fp32; this library stores states in
+ * fp32, so its state pool is the state_elem_bytes = 4 figure). Negative or
+ * inconsistent sizes, or a result beyond 2^64 - 1, give HYATTN_ERR_INVALID_ARG
+ * and leave *out untouched. */
+hyattn_status hyattn_estimate_memory(const int32_t* layer_types, int n_layers, int H, int H_kv,
+                                     int D, const int32_t* context_lens, int n_requests,
+                                     int kv_elem_bytes, int state_elem_bytes,
+                                     hyattn_memory_estimate* out);
 
 #ifdef __cplusplus
 }

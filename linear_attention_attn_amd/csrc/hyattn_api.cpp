@@ -435,6 +435,50 @@ hyattn_status hyattn_paged_prefill(const void* q, void* o, const void* k_pool, c
 }
 
 // ---------------------------------------------------------------- hybrid step --
+hyattn_status hyattn_estimate_memory(const int32_t* layer_types, int n_layers, int H, int H_kv,
+                                     int D, const int32_t* context_lens, int n_requests,
+                                     int kv_elem_bytes, int state_elem_bytes,
+                                     hyattn_memory_estimate* out) {
+  if (!out) return fail(HYATTN_ERR_INVALID_ARG, "out is NULL");
+  if (n_layers < 0 || n_requests < 0 || H < 0 || H_kv < 0 || D < 0 || kv_elem_bytes < 0 ||
+      state_elem_bytes < 0)
+    return fail(HYATTN_ERR_INVALID_ARG, "negative size");
+  if ((n_layers > 0 && !layer_types) || (n_requests > 0 && !context_lens))
+    return fail(HYATTN_ERR_INVALID_ARG, "layer_types or context_lens is NULL");
+  int n_full = 0, n_lin = 0;
+  for (int i = 0; i < n_layers; ++i) {
+    if (layer_types[i] == HYATTN_LAYER_FULL)
+      ++n_full;
+    else if (layer_types[i] == HYATTN_LAYER_LINEAR)
+      ++n_lin;
+    else
+      return fail(HYATTN_ERR_UNSUPPORTED_LAYER, "layer %d: attention type %d is not supported", i,
+                  layer_types[i]);
+  }
+  typedef unsigned __int128 u128;
+  u128 tokens = 0, blocks = 0;
+  for (int r = 0; r < n_requests; ++r) {
+    if (context_lens[r] < 0) return fail(HYATTN_ERR_INVALID_ARG, "context_lens[%d] < 0", r);
+    tokens += (u128)context_lens[r];
+    blocks += ((u128)context_lens[r] + HYATTN_BLOCK_TOKENS - 1) / HYATTN_BLOCK_TOKENS;
+  }
+  const u128 per_token = (u128)2 * (unsigned)n_full * (unsigned)H_kv * (unsigned)D * (unsigned)kv_elem_bytes;
+  const u128 kv = per_token * tokens;
+  const u128 kv_paged = per_token * blocks * HYATTN_BLOCK_TOKENS;
+  const u128 state = (u128)(unsigned)n_lin * (unsigned)H * (unsigned)D * (unsigned)D *
+                     (unsigned)n_requests * (unsigned)state_elem_bytes;
+  const u128 lim = (u128)UINT64_MAX;
+  if (kv > lim || kv_paged > lim || state > lim || blocks > lim)
+    return fail(HYATTN_ERR_INVALID_ARG, "estimate exceeds 2^64 - 1 bytes");
+  out->kv_bytes = (uint64_t)kv;
+  out->kv_paged_bytes = (uint64_t)kv_paged;
+  out->kv_blocks = (uint64_t)blocks;
+  out->state_bytes = (uint64_t)state;
+  out->n_full_layers = n_full;
+  out->n_linear_layers = n_lin;
+  return ok();
+}
+
 size_t hyattn_hybrid_workspace_bytes(const hyattn_batch* b) {
   if (!b || b->n_decode < 0) return 0;
   return hy::decode_workspace_bytes(b->n_decode, b->H, b->D, b->max_context);

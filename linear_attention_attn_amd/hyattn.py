@@ -32,6 +32,7 @@ EXPORTS = (
     "hyattn_state_pool_state_ptr", "hyattn_linear_prefill_chunked", "hyattn_linear_decode",
     "hyattn_paged_append", "hyattn_paged_decode_workspace_bytes", "hyattn_paged_decode",
     "hyattn_paged_prefill", "hyattn_hybrid_workspace_bytes", "hyattn_hybrid_step",
+    "hyattn_estimate_memory",
 )
 
 
@@ -57,6 +58,12 @@ class Batch(C.Structure):
                 ("H", C.c_int), ("H_kv", C.c_int), ("D", C.c_int), ("chunk_size", C.c_int),
                 ("scale", C.c_float), ("dtype", C.c_int), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t)]
+
+
+class MemoryEstimate(C.Structure):
+    _fields_ = [("kv_bytes", C.c_uint64), ("kv_paged_bytes", C.c_uint64),
+                ("kv_blocks", C.c_uint64), ("state_bytes", C.c_uint64),
+                ("n_full_layers", C.c_int), ("n_linear_layers", C.c_int)]
 
 
 _lib = None
@@ -98,6 +105,7 @@ def load():
                                  st),
         "hyattn_hybrid_workspace_bytes": ([C.POINTER(Batch)], sz),
         "hyattn_hybrid_step": ([vp, i, C.POINTER(LayerIO), C.POINTER(Batch), vp, vp], st),
+        "hyattn_estimate_memory": ([vp, i, i, i, i, vp, i, i, i, C.POINTER(MemoryEstimate)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -262,3 +270,15 @@ def hyattn_hybrid_step(layer_types, n_layers, layers, batch: Batch, pool, stream
     arr = layers if isinstance(layers, C.Array) else make_layers(layers)
     _check(load().hyattn_hybrid_step(C.cast(lt, C.c_void_p), n_layers, arr, C.byref(batch), pool,
                                      _stream(stream)))
+
+
+def hyattn_estimate_memory(layer_types, H, H_kv, D, context_lens, kv_elem_bytes, state_elem_bytes):
+    """Host-only memory estimate; returns a dict of the hyattn_memory_estimate fields."""
+    import numpy as np
+    lt = np.ascontiguousarray(layer_types, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    out = MemoryEstimate()
+    _check(load().hyattn_estimate_memory(ptr(lt) if lt.size else None, int(lt.size), int(H), int(H_kv),
+                                         int(D), ptr(cl) if cl.size else None, int(cl.size),
+                                         int(kv_elem_bytes), int(state_elem_bytes), C.byref(out)))
+    return {name: int(getattr(out, name)) for name, _ in MemoryEstimate._fields_}

@@ -234,6 +234,34 @@ def paged_attention(q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, sc
     return out
 
 
+# ------------------------------------------------------- memory estimate --
+def memory_estimate(layer_types, H, H_kv, D, context_lens, kv_elem_bytes, state_elem_bytes):
+    """Device bytes of the two state kinds (P2 §3.3, P2 §2.1), exact integers.
+
+    Full layers: K and V of every cached token, 2 * L_full * H_kv * D * S *
+    elem bytes summed over requests (P2 §3.3's 2 x L x H x D x S x batch x
+    dtype with per-request S); the paged pool holds whole 16-token blocks, so
+    each S rounds up to a multiple of 16 there (P2 §2.1). Linear layers: one
+    H x D x D state per request, L_lin * H * D * D * batch * elem bytes,
+    independent of S. layer_types are names or codes as in
+    ``parse_layer_types``.
+    """
+    types = parse_layer_types(layer_types)
+    n_full = sum(1 for t in types if t == 1)
+    n_lin = sum(1 for t in types if t == 0)
+    ctx = [int(c) for c in context_lens]
+    if any(c < 0 for c in ctx):
+        raise ValueError("negative context length")
+    tokens = sum(ctx)
+    blocks = sum(-(-c // BLOCK) for c in ctx)
+    per_token = 2 * n_full * H_kv * D * kv_elem_bytes
+    return {"kv_bytes": per_token * tokens,
+            "kv_paged_bytes": per_token * blocks * BLOCK,
+            "kv_blocks": blocks,
+            "state_bytes": n_lin * H * D * D * len(ctx) * state_elem_bytes,
+            "n_full_layers": n_full, "n_linear_layers": n_lin}
+
+
 # -------------------------------------------------------- state-pool slots --
 class SlotAllocator:
     """Reference simulation of the state-pool slot free list.

@@ -168,3 +168,34 @@ def test_layer_type_spellings_map_like_the_oracle():
     assert layer_types.parse(["linear", "full"]) == ref.parse_layer_types(["linear", "full"])
     with pytest.raises(ValueError):
         layer_types.parse(["mamba"])
+
+
+def test_memory_estimate_matches_the_oracle_exactly():
+    """hyattn_estimate_memory (host) == the oracle's integer formula (P2 §3.3)."""
+    rng = np.random.default_rng(31)
+    names = {0: "linear", 1: "full"}
+    for trial in range(25):
+        n = int(rng.integers(0, 40))
+        codes = rng.integers(0, 2, size=n).tolist()
+        ctx = rng.integers(0, 200000, size=int(rng.integers(0, 300))).tolist()
+        H, H_kv, D = int(rng.choice([8, 32, 64])), int(rng.choice([1, 8, 32])), int(rng.choice([64, 128]))
+        kvb, stb = int(rng.choice([2, 4])), int(rng.choice([2, 4]))
+        got = hy.hyattn_estimate_memory(codes, H, H_kv, D, ctx, kvb, stb)
+        want = ref.memory_estimate([names[c] for c in codes], H, H_kv, D, ctx, kvb, stb)
+        assert got == want, (trial, got, want)
+    # the state pool of this library is the fp32 figure
+    e = hy.hyattn_estimate_memory([0] * 24 + [1] * 8, 32, 8, 128, [5] * 256, 2, 4)
+    assert e["state_bytes"] == hy.hyattn_state_pool_bytes(24, 256, 32, 128)
+
+
+def test_memory_estimate_errors():
+    with pytest.raises(hy.HyattnError) as ex:
+        hy.hyattn_estimate_memory([0, 7], 32, 8, 128, [1], 2, 4)
+    assert ex.value.status == hy.ERR_UNSUPPORTED_LAYER
+    with pytest.raises(hy.HyattnError) as ex:
+        hy.hyattn_estimate_memory([0, 1], 32, 8, 128, [1, -1], 2, 4)
+    assert ex.value.status == hy.ERR_INVALID_ARG
+    with pytest.raises(hy.HyattnError) as ex:  # beyond 2^64 - 1 bytes
+        hy.hyattn_estimate_memory([1] * 100000, 2**31 - 1, 2**31 - 1, 2**31 - 1, [2**31 - 1] * 4, 4, 4)
+    assert ex.value.status == hy.ERR_INVALID_ARG
+

@@ -372,3 +372,47 @@ def test_hybrid_step_composes_the_layer_ops():
             for h in range(H):
                 e = _dense_attention(layers[1]["q"][cu_all[r] + i, h], K[:n], V[:n], 0.35)
                 assert _rel(outs[1][cu_all[r] + i, h], e) < 1e-12
+
+
+# ------------------------------------------------------- memory estimate --
+def _golden(name):
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    vals = {}
+    for line in open(path, encoding="utf-8"):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = (x.strip() for x in line.split("="))
+            vals[k] = int(v)
+    return vals
+
+
+def test_memory_estimate_reproduces_the_pages_worked_example():
+    """P2 §3.3 prints ~103 GB of full-layer KV and ~67 MB of linear state for
+    32 layers (24 full, 8 linear), H = 32, D = 128, S = 32768, batch 8, bf16."""
+    g = _golden("p2_s3_3_memory_example.txt")
+    types = ["full"] * g["n_full_layers"] + ["linear"] * g["n_linear_layers"]
+    assert len(types) == g["n_layers"]
+    est = ref.memory_estimate(types, g["heads"], g["heads"], g["head_dim"],
+                              [g["seq_len"]] * g["batch"], g["dtype_bytes"], g["dtype_bytes"])
+    assert round(est["kv_bytes"] / 1e9) == g["printed_full_kv_gb"]
+    assert round(est["state_bytes"] / 1e6) == g["printed_linear_state_mb"]
+    assert est["kv_paged_bytes"] == est["kv_bytes"]  # 32768 is a whole number of blocks
+    assert est["kv_blocks"] == g["batch"] * g["seq_len"] // 16
+
+
+def test_memory_estimate_invariants():
+    """Block rounding, independence of the state from the length, linearity."""
+    types = ["linear", "full", "linear", "linear"]
+    per_tok = 2 * 1 * 8 * 128 * 2
+    e = ref.memory_estimate(types, 32, 8, 128, [1], 2, 4)
+    assert e["kv_bytes"] == per_tok and e["kv_paged_bytes"] == 16 * per_tok and e["kv_blocks"] == 1
+    e2 = ref.memory_estimate(types, 32, 8, 128, [100000], 2, 4)
+    assert e2["state_bytes"] == e["state_bytes"] == 3 * 32 * 128 * 128 * 4
+    e3 = ref.memory_estimate(types, 32, 8, 128, [17, 32, 0], 2, 4)
+    assert e3["kv_blocks"] == 2 + 2 + 0 and e3["kv_bytes"] == 49 * per_tok
+    assert e3["state_bytes"] == 3 * e["state_bytes"]
+    assert ref.memory_estimate(["linear"], 32, 8, 128, [4096], 2, 4)["kv_bytes"] == 0
+    with pytest.raises(ValueError):
+        ref.memory_estimate(["sliding"], 32, 8, 128, [1], 2, 4)
+
