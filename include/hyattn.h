@@ -269,6 +269,36 @@ hyattn_status hyattn_estimate_memory(const int32_t* layer_types, int n_layers, i
                                      int kv_elem_bytes, int state_elem_bytes,
                                      hyattn_memory_estimate* out);
 
+/* ---------------------------------------------------------------------------
+ * Length-bucketed batch formation (page "推理框架适配Hybrid Model：KV Cache管理与
+ * 算子调度实战", §2.4 on scheduling: a full layer's cost grows with the longest
+ * sequence of its batch, a linear layer's does not, so requests of similar
+ * length are batched together). Host only, no GPU.
+ *
+ * The cost of a batch is its padded size: requests x its longest length.
+ * Requests are ordered by length (ties by index), and that order is cut into
+ * consecutive batches, each taking requests while its padded size stays
+ * <= max_padded_tokens and its request count <= max_requests. This gives the
+ * fewest batches any grouping under the two limits can have (a grouping can
+ * always be rearranged into consecutive runs of the sorted order without
+ * raising any batch's longest length).
+ *
+ *   lengths           host int32[n]: tokens of each request (>= 0).
+ *   max_padded_tokens per-batch limit on count * longest length (>= 1); a
+ *                     single request longer than it is HYATTN_ERR_INVALID_ARG
+ *                     (prefill such a request in chunks first).
+ *   max_requests      per-batch limit on the request count (>= 1).
+ *   order             host int32[n] out: request indices, batch by batch.
+ *   batch_offsets     host int32[n+1] out: batch b holds
+ *                     order[batch_offsets[b] .. batch_offsets[b+1]-1];
+ *                     entries past *n_batches are left untouched.
+ *   n_batches         host out: number of batches (0 for n = 0).
+ * Invalid arguments give HYATTN_ERR_INVALID_ARG and leave the outputs
+ * untouched. */
+hyattn_status hyattn_bucket_by_length(const int32_t* lengths, int n, int64_t max_padded_tokens,
+                                      int max_requests, int32_t* order, int32_t* batch_offsets,
+                                      int* n_batches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -476,6 +477,42 @@ hyattn_status hyattn_estimate_memory(const int32_t* layer_types, int n_layers, i
   out->state_bytes = (uint64_t)state;
   out->n_full_layers = n_full;
   out->n_linear_layers = n_lin;
+  return ok();
+}
+
+hyattn_status hyattn_bucket_by_length(const int32_t* lengths, int n, int64_t max_padded_tokens,
+                                      int max_requests, int32_t* order, int32_t* batch_offsets,
+                                      int* n_batches) {
+  if (n < 0) return fail(HYATTN_ERR_INVALID_ARG, "n < 0");
+  if (!n_batches || !batch_offsets || (n > 0 && (!lengths || !order)))
+    return fail(HYATTN_ERR_INVALID_ARG, "NULL argument");
+  if (max_padded_tokens < 1 || max_requests < 1)
+    return fail(HYATTN_ERR_INVALID_ARG, "max_padded_tokens and max_requests must be >= 1");
+  for (int r = 0; r < n; ++r) {
+    if (lengths[r] < 0) return fail(HYATTN_ERR_INVALID_ARG, "lengths[%d] < 0", r);
+    if (lengths[r] > max_padded_tokens)
+      return fail(HYATTN_ERR_INVALID_ARG, "request %d: %d tokens exceed max_padded_tokens %lld", r,
+                  lengths[r], (long long)max_padded_tokens);
+  }
+  std::vector<int32_t> idx(n);
+  for (int r = 0; r < n; ++r) idx[r] = r;
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int32_t a, int32_t b) { return lengths[a] < lengths[b]; });
+  // Sorted ascending, the request being added is always the batch's longest.
+  std::vector<int32_t> offs{0};
+  int64_t count = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t len = lengths[idx[i]];
+    if (count > 0 && (count + 1 > max_requests || (count + 1) * len > max_padded_tokens)) {
+      offs.push_back(i);
+      count = 0;
+    }
+    ++count;
+  }
+  if (n > 0) offs.push_back(n);
+  for (int i = 0; i < n; ++i) order[i] = idx[i];
+  for (size_t b = 0; b < offs.size(); ++b) batch_offsets[b] = offs[b];
+  *n_batches = (int)offs.size() - 1;
   return ok();
 }
 

@@ -33,6 +33,7 @@ EXPORTS = (
     "hyattn_paged_append", "hyattn_paged_decode_workspace_bytes", "hyattn_paged_decode",
     "hyattn_paged_prefill", "hyattn_hybrid_workspace_bytes", "hyattn_hybrid_step",
     "hyattn_estimate_memory",
+    "hyattn_bucket_by_length",
 )
 
 
@@ -106,6 +107,7 @@ def load():
         "hyattn_hybrid_workspace_bytes": ([C.POINTER(Batch)], sz),
         "hyattn_hybrid_step": ([vp, i, C.POINTER(LayerIO), C.POINTER(Batch), vp, vp], st),
         "hyattn_estimate_memory": ([vp, i, i, i, i, vp, i, i, i, C.POINTER(MemoryEstimate)], st),
+        "hyattn_bucket_by_length": ([vp, i, i64, i, vp, vp, C.POINTER(C.c_int)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -282,3 +284,17 @@ def hyattn_estimate_memory(layer_types, H, H_kv, D, context_lens, kv_elem_bytes,
                                          int(D), ptr(cl) if cl.size else None, int(cl.size),
                                          int(kv_elem_bytes), int(state_elem_bytes), C.byref(out)))
     return {name: int(getattr(out, name)) for name, _ in MemoryEstimate._fields_}
+
+
+def hyattn_bucket_by_length(lengths, max_padded_tokens, max_requests):
+    """Host-only length-bucketed batch formation; returns a list of batches,
+    each a list of request indices."""
+    import numpy as np
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    order = np.zeros(max(ln.size, 1), np.int32)
+    offs = np.zeros(ln.size + 1, np.int32)
+    nb = C.c_int(0)
+    _check(load().hyattn_bucket_by_length(ptr(ln) if ln.size else None, int(ln.size),
+                                          int(max_padded_tokens), int(max_requests), ptr(order),
+                                          ptr(offs), C.byref(nb)))
+    return [order[offs[b]:offs[b + 1]].tolist() for b in range(nb.value)]

@@ -262,6 +262,35 @@ def memory_estimate(layer_types, H, H_kv, D, context_lens, kv_elem_bytes, state_
             "n_full_layers": n_full, "n_linear_layers": n_lin}
 
 
+# ------------------------------------------------- length-bucketed batches --
+def bucket_by_length(lengths, max_padded_tokens, max_requests):
+    """Group requests of similar length into batches (P2 §2.4 scheduling).
+
+    Reading of P2 §2.4: a full layer pays for its batch's longest sequence
+    (padding), a linear layer does not, so batches are formed from requests of
+    similar length. A batch's cost is its request count times its longest
+    length; each batch stays within max_padded_tokens of that cost and
+    max_requests requests. Requests are taken shortest first (ties by index)
+    and a new batch starts when the next request would break a limit.
+    Returns a list of batches, each a list of request indices.
+    """
+    lengths = [int(x) for x in lengths]
+    if max_padded_tokens < 1 or max_requests < 1:
+        raise ValueError("limits must be >= 1")
+    if any(x < 0 or x > max_padded_tokens for x in lengths):
+        raise ValueError("a length is negative or exceeds max_padded_tokens")
+    ranked = sorted(range(len(lengths)), key=lambda r: (lengths[r], r))
+    batches = []
+    for r in ranked:
+        cur = batches[-1] if batches else None
+        if cur is not None and len(cur) + 1 <= max_requests and \
+                (len(cur) + 1) * max(lengths[j] for j in cur + [r]) <= max_padded_tokens:
+            cur.append(r)
+        else:
+            batches.append([r])
+    return batches
+
+
 # -------------------------------------------------------- state-pool slots --
 class SlotAllocator:
     """Reference simulation of the state-pool slot free list.

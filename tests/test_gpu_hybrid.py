@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
     dict(n_layers=8, prefill_lens=(1, 130, 16), decode_ctx=(2, 600, 33, 1), chunk=64),
     dict(dtype="f32", D=64, H=4, Hkv=4, prefill_lens=(256,), decode_ctx=(257,), chunk=64,
          n_layers=2, pattern=("linear", "full")),                  # the tiny fp32 case
-    dict(n_prefill=0) if False else dict(prefill_lens=(), decode_ctx=(5, 900)),
+    dict(prefill_lens=(), decode_ctx=(5, 900)),                    # decode only
     dict(prefill_lens=(33, 8), decode_ctx=()),
 ])
 def test_hybrid_step_matches_oracle(kw):

@@ -199,3 +199,32 @@ def test_memory_estimate_errors():
         hy.hyattn_estimate_memory([1] * 100000, 2**31 - 1, 2**31 - 1, 2**31 - 1, [2**31 - 1] * 4, 4, 4)
     assert ex.value.status == hy.ERR_INVALID_ARG
 
+
+
+def test_bucket_by_length_matches_the_oracle_exactly():
+    rng = np.random.default_rng(12)
+    for trial in range(40):
+        n = int(rng.integers(0, 300))
+        mix = rng.integers(0, 3, n)  # short, medium and long requests
+        lengths = np.where(mix == 0, rng.integers(0, 64, n),
+                           np.where(mix == 1, rng.integers(64, 2048, n), rng.integers(2048, 32768, n)))
+        T = int(rng.integers(max(int(lengths.max(initial=0)), 1), 200000))
+        R = int(rng.integers(1, 64))
+        assert hy.hyattn_bucket_by_length(lengths, T, R) == ref.bucket_by_length(lengths, T, R)
+
+
+def test_bucket_by_length_errors_leave_outputs_untouched():
+    L = hy.load()
+    ln = np.array([3, 11], np.int32)
+    order = np.full(2, -7, np.int32)
+    offs = np.full(3, -7, np.int32)
+    nb = C.c_int(-7)
+    for T, R, lens in ((10, 4, ln), (0, 4, ln[:1]), (10, 0, ln[:1]),
+                       (10, 4, np.array([2, -1], np.int32))):
+        st = L.hyattn_bucket_by_length(lens.ctypes.data, int(lens.size), T, R, order.ctypes.data,
+                                       offs.ctypes.data, C.byref(nb))
+        assert st == hy.ERR_INVALID_ARG
+        assert (order == -7).all() and (offs == -7).all() and nb.value == -7
+    assert L.hyattn_bucket_by_length(None, 0, 5, 5, None, offs.ctypes.data, C.byref(nb)) == 0
+    assert nb.value == 0 and offs[0] == 0
+    assert L.hyattn_bucket_by_length(None, -1, 5, 5, None, offs.ctypes.data, C.byref(nb)) != 0

@@ -374,6 +374,27 @@ def test_hybrid_step_composes_the_layer_ops():
                 assert _rel(outs[1][cu_all[r] + i, h], e) < 1e-12
 
 
+def test_hybrid_step_two_steps_equal_one_step():
+    """P2 §2.4: a prompt cut into two chunks, with K/V kept in the pools and the
+    linear state carried between them (same cut for every layer), gives what
+    one step over the whole prompt gives; a decode request's two tokens over
+    two steps equal a two-token chunk with its earlier context."""
+    from synth import hybrid
+    from tests import hybrid_run
+    case = hybrid.continuation_case(seed=3, n_layers=4, H=2, Hkv=1, D=16,
+                                    prompts=((40, 17), (9, 1), (33, 32)), decode_prior=(1, 45),
+                                    chunk=8, dtype="f32")
+    a_outs, a_states, a_pools = hybrid_run.run_oracle_steps(case)
+    b_outs, b_states, b_pools = hybrid_run.run_oracle_whole(case)
+    for a, b in zip(a_outs, b_outs):
+        assert _rel(a, b) < 1e-12
+    assert _rel(a_states, b_states) < 1e-12
+    for (ka, va), (kb, vb) in zip(a_pools, b_pools):
+        assert np.array_equal(ka.view(np.uint8), kb.view(np.uint8))  # unwritten rows are NaN
+        assert np.array_equal(va.view(np.uint8), vb.view(np.uint8))
+        assert not np.isnan(ka[case["layout"].block_tables[0, :2]]).any()
+
+
 # ------------------------------------------------------- memory estimate --
 def _golden(name):
     import os
@@ -416,3 +437,52 @@ def test_memory_estimate_invariants():
     with pytest.raises(ValueError):
         ref.memory_estimate(["sliding"], 32, 8, 128, [1], 2, 4)
 
+
+
+# ------------------------------------------------- length-bucketed batches --
+def _set_partitions(items):
+    if not items:
+        yield []
+        return
+    first, rest = items[0], items[1:]
+    for part in _set_partitions(rest):
+        yield [[first]] + part
+        for i in range(len(part)):
+            yield part[:i] + [[first] + part[i]] + part[i + 1:]
+
+
+def _feasible(batch, lengths, T, R):
+    return len(batch) <= R and len(batch) * max(lengths[r] for r in batch) <= T
+
+
+def test_bucket_by_length_handworked():
+    # sorted: 1 (r1), 3 (r2), 3 (r3), 5 (r0), 8 (r4); budget 9:
+    # 1,3,3 -> 3 x 3 = 9 fits; adding 5 gives 4 x 5 = 20; 5 then 8 gives 2 x 8 = 16
+    assert ref.bucket_by_length([5, 1, 3, 3, 8], 9, 4) == [[1, 2, 3], [0], [4]]
+    assert ref.bucket_by_length([5, 1, 3, 3, 8], 9, 2) == [[1, 2], [3], [0], [4]]
+    assert ref.bucket_by_length([4, 4, 4], 100, 1) == [[0], [1], [2]]
+    assert ref.bucket_by_length([7, 2, 9, 2], 10 ** 6, 8) == [[1, 3, 0, 2]]
+    assert ref.bucket_by_length([], 5, 5) == []
+    assert ref.bucket_by_length([0, 0, 0], 1, 2) == [[0, 1], [2]]
+    with pytest.raises(ValueError):
+        ref.bucket_by_length([3, 11], 10, 4)
+
+
+def test_bucket_by_length_fewest_batches_by_brute_force():
+    """Against every grouping of small request sets: the batches are valid,
+    cover each request once, and no valid grouping has fewer batches."""
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        n = int(rng.integers(1, 8))
+        lengths = [int(x) for x in rng.integers(0, 20, n)]
+        T = int(rng.integers(max(lengths + [1]), 60))
+        R = int(rng.integers(1, 5))
+        got = ref.bucket_by_length(lengths, T, R)
+        assert sorted(r for b in got for r in b) == list(range(n))
+        assert all(_feasible(b, lengths, T, R) for b in got)
+        best = min(len(p) for p in _set_partitions(list(range(n)))
+                   if all(_feasible(b, lengths, T, R) for b in p))
+        assert len(got) == best, (lengths, T, R, got)
+        # similar lengths together: batches are consecutive runs of the sorted order
+        flat = [r for b in got for r in b]
+        assert flat == sorted(range(n), key=lambda r: (lengths[r], r))
