@@ -25,7 +25,8 @@
  *     already contains k_t (x) v_t;
  *   - S[i][j] += k[i] * v[j]  (row = key dim, column = value dim) and
  *     o[j] = sum_i q[i] * S[i][j];
- *   - identity feature map, no normaliser, no decay, no extra scale;
+ *   - identity feature map, no normaliser, no extra scale; no decay in the
+ *     plain layer (the gated variant below adds a per-token forget factor);
  *   - logical token p of a request lives in physical block table[p / 16] at
  *     offset p % 16; a pool is laid out [n_blocks][H_kv][16][D];
  *   - query head h reads KV head h / (H_q / H_kv).
@@ -166,6 +167,98 @@ void ref_linear_closed_form(int T, int D, int dt, const void* q, const void* k,
       }
       S[(int64_t)i * D + j] += acc;
     }
+}
+
+/* ---------------------------------------------------------------------------
+ * Decayed (gated) linear attention: the state recurrence with a forget factor,
+ * the nearest relative of the linear layer among the state-update variants the
+ * pages point to (P2 §1.3: Mamba- and RWKV-style layers; P1 §2.1: a state
+ * carried as h_t = f(h_{t-1}, x_t)). Token t brings a log forget factor
+ * g_t <= 0 for its head, gamma_t = exp(g_t), and
+ *     S_t = gamma_t S_{t-1} + k_t (x) v_t,   out_t = q_t . S_t.
+ * g_t = 0 everywhere is the plain linear layer above. g of token t is read at
+ * element goff + t * ldg of g (type dt_g).
+ */
+void ref_linear_gated_recurrent(int T, int D, int dt, const void* q, const void* k,
+                                const void* v, int64_t off, int64_t ldx, int dt_g,
+                                const void* g, int64_t goff, int64_t ldg, double* S,
+                                double* o, int64_t ldo) {
+  for (int t = 0; t < T; ++t) {
+    const int64_t row = off + (int64_t)t * ldx;
+    const double gamma = exp(ld(g, dt_g, goff + (int64_t)t * ldg));
+    for (int i = 0; i < D; ++i) {
+      const double ki = ld(k, dt, row + i);
+      for (int j = 0; j < D; ++j) {
+        double* s = &S[(int64_t)i * D + j];
+        *s = gamma * *s + ki * ld(v, dt, row + j);
+      }
+    }
+    for (int j = 0; j < D; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < D; ++i) acc += ld(q, dt, row + i) * S[(int64_t)i * D + j];
+      o[(int64_t)t * ldo + j] = acc;
+    }
+  }
+}
+
+/*
+ * The same, chunk by chunk (P2 §2.4). Within a chunk starting from S0, let
+ * L_a = g_0 + ... + g_a (positions relative to the chunk). Unrolling the
+ * recurrence gives
+ *     out_a = exp(L_a) q_a . S0 + sum_{b <= a} exp(L_a - L_b) (q_a . k_b) v_b
+ *     S0   <- exp(L_last) S0 + sum_b exp(L_last - L_b) k_b (x) v_b
+ * All factors are exp of a sum of g's, so none exceeds 1.
+ */
+void ref_linear_gated_chunked(int T, int C, int D, int dt, const void* q, const void* k,
+                              const void* v, int64_t off, int64_t ldx, int dt_g,
+                              const void* g, int64_t goff, int64_t ldg, double* S,
+                              double* o, int64_t ldo) {
+  if (C < 1) C = 1;
+  double* P = (double*)malloc(sizeof(double) * (size_t)C * (size_t)C);
+  double* L = (double*)malloc(sizeof(double) * (size_t)C);
+  for (int c0 = 0; c0 < T; c0 += C) {
+    const int n = (T - c0 < C) ? (T - c0) : C;
+    double run = 0.0;
+    for (int a = 0; a < n; ++a) {
+      run += ld(g, dt_g, goff + (int64_t)(c0 + a) * ldg);
+      L[a] = run;
+    }
+    for (int a = 0; a < n; ++a)
+      for (int b = 0; b < n; ++b) {
+        double s = 0.0;
+        if (b <= a) {
+          const int64_t ra = off + (int64_t)(c0 + a) * ldx;
+          const int64_t rb = off + (int64_t)(c0 + b) * ldx;
+          for (int i = 0; i < D; ++i) s += ld(q, dt, ra + i) * ld(k, dt, rb + i);
+          s *= exp(L[a] - L[b]);
+        }
+        P[(int64_t)a * C + b] = s;
+      }
+    for (int a = 0; a < n; ++a) {
+      const int64_t ra = off + (int64_t)(c0 + a) * ldx;
+      const double da = exp(L[a]);
+      for (int j = 0; j < D; ++j) {
+        double inter = 0.0;
+        for (int i = 0; i < D; ++i) inter += ld(q, dt, ra + i) * S[(int64_t)i * D + j];
+        double acc = da * inter;
+        for (int b = 0; b <= a; ++b)
+          acc += P[(int64_t)a * C + b] * ld(v, dt, off + (int64_t)(c0 + b) * ldx + j);
+        o[(int64_t)(c0 + a) * ldo + j] = acc;
+      }
+    }
+    const double dn = exp(L[n - 1]);
+    for (int i = 0; i < D; ++i)
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int b = 0; b < n; ++b) {
+          const int64_t rb = off + (int64_t)(c0 + b) * ldx;
+          acc += exp(L[n - 1] - L[b]) * ld(k, dt, rb + i) * ld(v, dt, rb + j);
+        }
+        S[(int64_t)i * D + j] = dn * S[(int64_t)i * D + j] + acc;
+      }
+  }
+  free(L);
+  free(P);
 }
 
 /* ---------------------------------------------------------------------------

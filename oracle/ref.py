@@ -58,6 +58,12 @@ def lib():
             L.ref_linear_chunked.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, vp, vp, vp,
                                              i64, i64, dp, dp, i64]
             L.ref_linear_chunked.restype = None
+            for name in ("ref_linear_gated_recurrent", "ref_linear_gated_chunked"):
+                f = getattr(L, name)
+                head = [C.c_int, C.c_int] if name.endswith("chunked") else [C.c_int]
+                f.argtypes = head + [C.c_int, C.c_int, vp, vp, vp, i64, i64, C.c_int, vp, i64,
+                                     i64, dp, dp, i64]
+                f.restype = None
             L.ref_kv_offset.argtypes = [i32p, C.c_int, C.c_int, C.c_int, C.c_int]
             L.ref_kv_offset.restype = C.c_int64
             L.ref_paged_attention_query.argtypes = [C.c_int, C.c_int, vp, i64, C.c_int, vp, vp,
@@ -103,12 +109,16 @@ def _pmap(fn, items, threads=None):
 
 
 # ----------------------------------------------------------- linear layers --
-def linear_unit(form: str, q, k, v, S, token0: int, T: int, head: int, chunk: int = 0):
+def linear_unit(form: str, q, k, v, S, token0: int, T: int, head: int, chunk: int = 0,
+                log_gamma=None):
     """Run one (request, head) unit on packed [N_tok][H][D] inputs.
 
     form: "recurrent" (the token recurrence), "chunked" (P2 §2.4 chunk form with
     chunk size ``chunk``) or "closed" (whole-sequence closed form).
     S: float64 [D][D] prior state, updated in place. Returns out [T][D] f64.
+    log_gamma: None (plain layer) or the per-token log forget factors
+    [N_tok][H] (float32 or float64) of the gated variant; forms "recurrent"
+    and "chunked" only.
     """
     L = lib()
     assert q.dtype == k.dtype == v.dtype and q.shape == k.shape == v.shape
@@ -118,7 +128,18 @@ def linear_unit(form: str, q, k, v, S, token0: int, T: int, head: int, chunk: in
     o = np.zeros((max(T, 1), D), dtype=np.float64)
     off, ldx = (token0 * H + head) * D, H * D
     args = (_dt(q), _ptr(q), _ptr(k), _ptr(v), off, ldx, _dptr(S), _dptr(o), D)
-    if T > 0:
+    if T > 0 and log_gamma is not None:
+        g = np.ascontiguousarray(log_gamma)
+        assert g.shape == (N, H) and g.dtype in (np.float32, np.float64)
+        gargs = (_dt(q), _ptr(q), _ptr(k), _ptr(v), off, ldx, _dt(g), _ptr(g), token0 * H + head,
+                 H, _dptr(S), _dptr(o), D)
+        if form == "recurrent":
+            L.ref_linear_gated_recurrent(T, D, *gargs)
+        elif form == "chunked":
+            L.ref_linear_gated_chunked(T, int(chunk), D, *gargs)
+        else:
+            raise ValueError(form)
+    elif T > 0:
         if form == "recurrent":
             L.ref_linear_recurrent(T, D, *args)
         elif form == "chunked":
@@ -131,12 +152,13 @@ def linear_unit(form: str, q, k, v, S, token0: int, T: int, head: int, chunk: in
 
 
 def linear_prefill(q, k, v, cu_seqlens, states, chunk: int = 0, form: str = "chunked",
-                   units=None, threads=None):
+                   units=None, threads=None, log_gamma=None):
     """Prefill of packed requests (P2 §2.1 recurrence, §2.4 chunking).
 
     states: float64 [n_req][H][D][D], updated in place (the slot's state on
     entry: zero at request start). Returns out float64 [N][H][D] (rows of
-    units not listed in ``units`` stay zero).
+    units not listed in ``units`` stay zero). log_gamma [N][H]: the gated
+    variant's per-token log forget factors (None: plain layer).
     """
     N, H, D = q.shape
     cu = np.asarray(cu_seqlens, dtype=np.int64)
@@ -149,7 +171,7 @@ def linear_prefill(q, k, v, cu_seqlens, states, chunk: int = 0, form: str = "chu
         r, h = u
         S = np.ascontiguousarray(states[r, h])
         t0, T = int(cu[r]), int(cu[r + 1] - cu[r])
-        o = linear_unit(form, q, k, v, S, t0, T, h, chunk)
+        o = linear_unit(form, q, k, v, S, t0, T, h, chunk, log_gamma)
         states[r, h] = S
         out[t0:t0 + T, h] = o
 
@@ -157,14 +179,16 @@ def linear_prefill(q, k, v, cu_seqlens, states, chunk: int = 0, form: str = "chu
     return out
 
 
-def linear_decode(q, k, v, states, units=None, threads=None):
-    """One decode step for B requests: per (r, h), S += k (x) v then o = q . S.
+def linear_decode(q, k, v, states, units=None, threads=None, log_gamma=None):
+    """One decode step for B requests: per (r, h), S += k (x) v then o = q . S
+    (gated variant: S <- exp(g) S + k (x) v with g = log_gamma[r][h]).
 
     q/k/v: [B][H][D]; states float64 [B][H][D][D] updated in place.
     """
     B, H, D = q.shape
     cu = np.arange(B + 1)
-    return linear_prefill(q, k, v, cu, states, form="recurrent", units=units, threads=threads)
+    return linear_prefill(q, k, v, cu, states, form="recurrent", units=units, threads=threads,
+                          log_gamma=log_gamma)
 
 
 # ------------------------------------------------------------- full layers --
@@ -346,7 +370,8 @@ def hybrid_step(layer_types, layers, batch, linear_states, kv_pools, threads=Non
 
     layer_types: list of 0 (linear) / 1 (full).
     layers[i]: dict with q, k, v (linear: [N][H][D]; full: q [N][Hq][D],
-      k, v [N][Hkv][D]).
+      k, v [N][Hkv][D]); a linear layer may add g, the gated variant's log
+      forget factors [N][H].
     batch: dict with prefill_cu (int [n_p+1]), n_decode, block_tables
       ([n_p+n_d][max_blocks]), context_lens ([n_p+n_d]), chunk, scale.
       Token rows: prefill requests first (packed), then one row per decode
@@ -370,14 +395,16 @@ def hybrid_step(layer_types, layers, batch, linear_states, kv_pools, threads=Non
             N, H, D = q.shape
             o = np.zeros((N, H, D))
             units_p = None if units_linear is None else [u for u in units_linear if u[0] < n_p]
+            g = io.get("g")  # gated variant: log forget factors [N][H]
             o[:Np] = linear_prefill(q[:Np], k[:Np], v[:Np], cu_p, st[:n_p],
                                     chunk=batch["chunk"], form="chunked", units=units_p,
-                                    threads=threads)[:Np]
+                                    threads=threads,
+                                    log_gamma=None if g is None else g[:Np])[:Np]
             units_d = None if units_linear is None else [(r - n_p, h) for r, h in units_linear
                                                          if r >= n_p]
             if n_d:
                 o[Np:] = linear_decode(q[Np:], k[Np:], v[Np:], st[n_p:], units=units_d,
-                                       threads=threads)
+                                       threads=threads, log_gamma=None if g is None else g[Np:])
             outs.append(o)
             li += 1
         elif t == 1:

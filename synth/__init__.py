@@ -65,6 +65,21 @@ def small_ints(rng: np.random.Generator, shape, lo: int, hi: int, dtype: str):
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
+def log_forget(rng: np.random.Generator, shape, p_one: float = 0.05):
+    """Per-token log forget factors g = log(gamma) <= 0, float32, shape [N][H].
+
+    Head h draws gamma = 1 - u * 2^-(2 + h % 8) with u ~ U(0, 1), so heads
+    range from fast forgetting (gamma in [0.75, 1]) to slow (gamma within
+    2^-9 of 1); a fraction p_one of the tokens has gamma = 1 exactly (g = 0).
+    """
+    N, H = shape
+    e = 2.0 + (np.arange(H) % 8)
+    gamma = 1.0 - rng.random((N, H)) * np.exp2(-e)[None, :]
+    g = np.log(gamma).astype(np.float32)
+    g[rng.random((N, H)) < p_one] = 0.0
+    return np.minimum(g, 0.0).astype(np.float32)
+
+
 def to_f32(a: np.ndarray) -> np.ndarray:
     """Widen a stored tensor (uint16 bf16 bits or float32) to float32."""
     return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, np.float32)

@@ -5,19 +5,21 @@ packed) and ``n_decode`` requests that bring one token each. Linear layers
 start prefill requests from a zero state and decode requests from a random
 prior state; full layers hold, for every decode request, its earlier
 context_len - 1 tokens in the paged pool (prefill requests start empty).
-Pure data generation: no arithmetic of the method.
+``gated`` adds log forget factors ``g`` [N][H] to every linear layer (the
+gated variant). Pure data generation: no arithmetic of the method.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import cu_lens, normal, paged_layout, BF16_NAN
+from . import cu_lens, log_forget, normal, paged_layout, BF16_NAN
 
 PATTERN = ("linear", "linear", "linear", "full")
 
 
 def small_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prefill_lens=(40, 70),
-               decode_ctx=(1, 17, 300), chunk=32, dtype="bf16", pattern=PATTERN, n_spare=4):
+               decode_ctx=(1, 17, 300), chunk=32, dtype="bf16", pattern=PATTERN, n_spare=4,
+               gated=False):
     rng = np.random.default_rng(seed)
     types = [pattern[i % len(pattern)] for i in range(n_layers)]
     n_p, n_d = len(prefill_lens), len(decode_ctx)
@@ -49,6 +51,8 @@ def small_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prefill_lens=(40, 70),
                     vp[b, :, :m] = normal(rng, (Hkv, m, D), 1.0, dtype)
             pools.append((kp, vp))
         layers.append(dict(q=q, k=k, v=v))
+        if gated and t == "linear":  # the gated variant's log forget factors
+            layers[-1]["g"] = log_forget(rng, (N, H))
     states = np.zeros((n_lin, n_p + n_d, H, D, D), np.float32)
     states[:, n_p:] = (rng.standard_normal((n_lin, n_d, H, D, D)) * 0.1).astype(np.float32)
     return dict(types=types, layers=layers, pools=pools, states=states, layout=lay, ctx=ctx,
@@ -60,7 +64,7 @@ def small_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prefill_lens=(40, 70),
 
 def continuation_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prompts=((40, 17), (70, 32), (129, 64)),
                       decode_prior=(1, 17, 300), decode_tokens=2, chunk=32, dtype="bf16",
-                      pattern=PATTERN, n_spare=4):
+                      pattern=PATTERN, n_spare=4, gated=False):
     """Requests whose new tokens are served over several steps.
 
     ``prompts`` holds (length, first) pairs: a prompt of ``length`` tokens with
@@ -71,7 +75,8 @@ def continuation_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prompts=((40, 17), 
     ``new`` give each request's cached and new token counts, ``split`` the
     tokens of each request that belong to the first step. Earlier tokens of
     decode requests sit in the pools, and their linear states are random;
-    prompts start from empty pools and zero states.
+    prompts start from empty pools and zero states. ``gated`` adds log forget
+    factors ``g`` [N][H] to every linear layer (the gated variant).
     """
     rng = np.random.default_rng(seed)
     types = [pattern[i % len(pattern)] for i in range(n_layers)]
@@ -105,6 +110,8 @@ def continuation_case(seed=0, n_layers=4, H=4, Hkv=2, D=128, prompts=((40, 17), 
                     vp[b, :, :m] = normal(rng, (Hkv, m, D), 1.0, dtype)
             pools.append((kp, vp))
         layers.append(dict(q=q, k=k, v=v))
+        if gated and t == "linear":  # the gated variant's log forget factors
+            layers[-1]["g"] = log_forget(rng, (N, H))
     states = np.zeros((n_lin, B, H, D, D), np.float32)
     has = prior > 0
     states[:, has] = (rng.standard_normal((n_lin, int(has.sum()), H, D, D)) * 0.1).astype(np.float32)

@@ -198,6 +198,9 @@ def run_oracle_steps(case):
         batch = dict(prefill_cu=sp["cu_p"], n_decode=sp["n_d"],
                      block_tables=case["layout"].block_tables, context_lens=sp["ctx"],
                      chunk=case["chunk"], scale=case["scale"])
+        for li, io in zip(layers, case["layers"]):
+            if "g" in io:
+                li["g"] = io["g"][sp["order"]]
         for i, o in enumerate(ref.hybrid_step(types, layers, batch, states, pools)):
             outs[i][sp["order"]] = o
     return outs, states, pools

@@ -71,6 +71,76 @@ def test_linear_matches_matrix_closed_form():
             assert _rel(S, expect_S) < RTOL, form
 
 
+# ------------------------------------------- gated (decayed) linear attention --
+def test_gated_with_zero_gates_is_the_plain_layer():
+    """g = 0 (gamma = 1) everywhere: the gated recurrence and chunked form give
+    the plain layer's results bit for bit."""
+    rng = np.random.default_rng(21)
+    N, H, D = 41, 2, 8
+    for dtype in ("f32", "bf16"):
+        q, k, v = _packed(rng, N, H, D, dtype)
+        g = np.zeros((N, H), np.float32)
+        S0 = rng.standard_normal((D, D)) * 0.3
+        for h in range(H):
+            for form, C in (("recurrent", 0), ("chunked", 1), ("chunked", 6), ("chunked", 64)):
+                Sa, Sb = S0.copy(), S0.copy()
+                a = ref.linear_unit(form, q, k, v, Sa, 0, N, h, C)
+                b = ref.linear_unit(form, q, k, v, Sb, 0, N, h, C, log_gamma=g)
+                assert np.array_equal(a, b) and np.array_equal(Sa, Sb), (dtype, form, C)
+
+
+def test_gated_matches_decay_masked_matrix_form():
+    """With L = cumsum(g): O = (tril(Q K^T) * exp(L_t - L_u)) V + exp(L_t) Q S0 and
+    S_T = exp(L_T) S0 + K^T diag(exp(L_T - L_u)) V, by numpy matmul; the
+    recurrence and the chunked form for every chunk size agree with it."""
+    rng = np.random.default_rng(22)
+    N, H, D = 45, 8, 6
+    q, k, v = _packed(rng, N, H, D, "f32")
+    g = synth.log_forget(rng, (N, H), p_one=0.2)
+    for h in range(H):
+        Q, K, V = (x[:, h].astype(np.float64) for x in (q, k, v))
+        L = np.cumsum(g[:, h].astype(np.float64))
+        M = np.tril(np.exp(L[:, None] - L[None, :]))
+        S0 = rng.standard_normal((D, D))
+        expect_o = ((Q @ K.T) * M) @ V + np.exp(L)[:, None] * (Q @ S0)
+        expect_S = np.exp(L[-1]) * S0 + K.T @ (np.exp(L[-1] - L)[:, None] * V)
+        for form, C in [("recurrent", 0)] + [("chunked", c) for c in (1, 2, 5, 16, 44, 45, 100)]:
+            S = S0.copy()
+            o = ref.linear_unit(form, q, k, v, S, 0, N, h, C, log_gamma=g)
+            assert _rel(o, expect_o) < RTOL, (form, C)
+            assert _rel(S, expect_S) < RTOL, (form, C)
+
+
+def test_gated_handworked():
+    """D = 2, S0 = I, gammas 1/2 then 1/4, worked by hand:
+    S1 = I/2 + k1 v1^T = [[2.5, 0], [2, 0.5]], o1 = row 0 of S1 = (2.5, 0);
+    S2 = S1/4 + k2 v2^T = [[0.625, 0], [1.5, 1.125]], o2 = row 1 of S2 = (1.5, 1.125)."""
+    q = np.array([[[1, 0]], [[0, 1]]], np.float64)
+    k = np.array([[[1, 1]], [[0, 1]]], np.float64)
+    v = np.array([[[2, 0]], [[1, 1]]], np.float64)
+    g = np.log(np.array([[0.5], [0.25]]))
+    for form, C in (("recurrent", 0), ("chunked", 1), ("chunked", 2)):
+        S = np.eye(2)
+        o = ref.linear_unit(form, q, k, v, S, 0, 2, 0, C, log_gamma=g)
+        assert np.allclose(o, [[2.5, 0], [1.5, 1.125]], rtol=0, atol=1e-14), form
+        assert np.allclose(S, [[0.625, 0], [1.5, 1.125]], rtol=0, atol=1e-14), form
+
+
+def test_gated_full_forgetting():
+    """gamma = 0 (g = -1000 underflows exp to 0): each token sees only itself,
+    o_t = (q_t . k_t) v_t, and the state ends as k_T (x) v_T."""
+    rng = np.random.default_rng(23)
+    N, H, D = 20, 1, 5
+    q, k, v = _packed(rng, N, H, D, "f32")
+    g = np.full((N, H), -1000.0)
+    Q, K, V = (x[:, 0].astype(np.float64) for x in (q, k, v))
+    for form, C in (("recurrent", 0), ("chunked", 7)):
+        S = rng.standard_normal((D, D))
+        o = ref.linear_unit(form, q, k, v, S, 0, N, 0, C, log_gamma=g)
+        assert _rel(o, np.sum(Q * K, axis=1)[:, None] * V) < RTOL
+        assert _rel(S, np.outer(K[-1], V[-1])) < RTOL
+
+
 def test_linear_exact_rational_bruteforce():
     """Tiny integer case, exact: o_t[j] = sum_i q_t[i] S0[i][j] + sum_{u<=t} (q_t.k_u) v_u[j]."""
     rng = np.random.default_rng(13)
@@ -374,7 +444,8 @@ def test_hybrid_step_composes_the_layer_ops():
                 assert _rel(outs[1][cu_all[r] + i, h], e) < 1e-12
 
 
-def test_hybrid_step_two_steps_equal_one_step():
+@pytest.mark.parametrize("gated", [False, True])
+def test_hybrid_step_two_steps_equal_one_step(gated):
     """P2 §2.4: a prompt cut into two chunks, with K/V kept in the pools and the
     linear state carried between them (same cut for every layer), gives what
     one step over the whole prompt gives; a decode request's two tokens over
@@ -383,7 +454,7 @@ def test_hybrid_step_two_steps_equal_one_step():
     from tests import hybrid_run
     case = hybrid.continuation_case(seed=3, n_layers=4, H=2, Hkv=1, D=16,
                                     prompts=((40, 17), (9, 1), (33, 32)), decode_prior=(1, 45),
-                                    chunk=8, dtype="f32")
+                                    chunk=8, dtype="f32", gated=gated)
     a_outs, a_states, a_pools = hybrid_run.run_oracle_steps(case)
     b_outs, b_states, b_pools = hybrid_run.run_oracle_whole(case)
     for a, b in zip(a_outs, b_outs):
