@@ -83,6 +83,8 @@ class Workload:
                         k=synth.device_normal_bf16((self.N, H, D), s, W["seed"] * 1000 + 3),
                         v=synth.device_normal_bf16((self.N, H, D), s, W["seed"] * 1000 + 4))
         self.lin["o"] = torch.empty_like(self.lin["q"])
+        # log forget factors of the gated linear variant (timed as a component only)
+        self.lin_g = synth.device_log_forget((self.N, H), W["seed"] * 1000 + 8)
         self.full = dict(q=synth.device_normal_bf16((self.N, H, D), 1.0, W["seed"] * 1000 + 5),
                          k=synth.device_normal_bf16((self.N, Hkv, D), 1.0, W["seed"] * 1000 + 6),
                          v=synth.device_normal_bf16((self.N, Hkv, D), 1.0, W["seed"] * 1000 + 7))
@@ -139,12 +141,14 @@ class Workload:
         qo = self.n_d * self.H * self.D * 2 * 2
         return kv + qo
 
-    def linear_decode_bytes(self):
-        return self.n_d * self.H * (2 * self.D * self.D * 4 + 4 * self.D * 2)
+    def linear_decode_bytes(self, gated=False):
+        # state read + write, q k v o rows (+ one fp32 gate per request-head)
+        return self.n_d * self.H * (2 * self.D * self.D * 4 + 4 * self.D * 2 + (4 if gated else 0))
 
-    def linear_prefill_flops(self):
+    def linear_prefill_flops(self, gated=False):
         C, D, T = W["chunk"], self.D, W["prefill_len"]
-        # per token-head: Q.S (2D^2) + S update (2D^2) + causal intra-chunk (C+1)D (QK^T and PV)
+        # per token-head: Q.S (2D^2) + S update (2D^2) + causal intra-chunk (C+1)D (QK^T and PV);
+        # the gates' scalings are elementwise and not counted
         per_tok = 4 * D * D + 2 * (C + 1) * D
         return self.n_p * T * self.H * per_tok
 
@@ -175,6 +179,12 @@ def component_times(wl, reps=3):
         "linear_decode": lambda: hy.hyattn_linear_decode(
             wl.pool, 0, row(lin["q"]), row(lin["k"]), row(lin["v"]), row(lin["o"]), wl.slots_d,
             n_d, hy.BF16),
+        "linear_prefill_gated": lambda: hy.hyattn_linear_prefill_chunked_gated(
+            wl.pool, 0, lin["q"], lin["k"], lin["v"], wl.lin_g, lin["o"], wl.cu_p, wl.slots_p,
+            n_p, W["chunk"], hy.BF16),
+        "linear_decode_gated": lambda: hy.hyattn_linear_decode_gated(
+            wl.pool, 0, row(lin["q"]), row(lin["k"]), row(lin["v"]), wl.lin_g[off:], row(lin["o"]),
+            wl.slots_d, n_d, hy.BF16),
         "paged_append": lambda: hy.hyattn_paged_append(
             full["k"], full["v"], kp, vp, wl.lay.n_blocks, wl.bt, wl.lay.max_blocks, wl.ctx_d,
             wl.cu_q, n_p + n_d, P, wl.Hkv, wl.D, hy.BF16),
@@ -433,6 +443,12 @@ def main():
             "paged_decode_hbm_frac": round(wl.decode_kv_bytes() / (pd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "linear_prefill_mfma_frac": round(wl.linear_prefill_flops() / (lp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "linear_prefill_hbm_frac": round(wl.linear_prefill_bytes() / (lp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "linear_prefill_gated_mfma_frac": round(
+                wl.linear_prefill_flops(gated=True) / (comp["linear_prefill_gated"] * 1e-3) / 1e12
+                / BF16_PEAK_TFLOPS, 4),
+            "linear_decode_gated_hbm_frac": round(
+                wl.linear_decode_bytes(gated=True) / (comp["linear_decode_gated"] * 1e-3) / 1e9
+                / HBM_PEAK_GBS, 4),
             "paged_prefill_mfma_frac": round(wl.paged_prefill_flops() / (comp["paged_prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "step_ms_from_components": round(comp["state_zero"] + n_lin * (lp + ld) + n_full * (
                 comp["paged_append"] + comp["paged_prefill"] + pd), 3),

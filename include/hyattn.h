@@ -141,6 +141,30 @@ hyattn_status hyattn_linear_decode(hyattn_state_pool* pool, int linear_layer, co
                                    const int32_t* slots_dev, int B, hyattn_dtype dtype,
                                    void* stream);
 
+/* Gated (decayed) linear layer: the same calls with a per-token forget factor,
+ * the nearest relative of the linear layer among the state-update variants
+ * the pages point to (P2 §1.3: Mamba- and RWKV-style layers; P1 §2.1: a
+ * state carried as h_t = f(h_{t-1}, x_t)). Token t of head h brings
+ * g = log_gamma[t][h] (device fp32 [N_tok][H]; decode: [B][H]), finite and
+ * <= 0 (checked in HYATTN_CHECK mode), and
+ *     S <- exp(g) S + k (x) v,   o = q . S.
+ * Chunked form, per chunk with L_a = g_0 + ... + g_a over the chunk:
+ *     O_c = diag(exp(L)) Q_c S + (tril(Q_c K_c^T) * exp(L_a - L_b)) V_c,
+ *     S  <- exp(L_last) S + K_c^T diag(exp(L_last - L_b)) V_c.
+ * log_gamma = 0 everywhere gives the plain layer's results. Other arguments,
+ * limits and errors as for the plain calls; log_gamma must not be NULL. */
+hyattn_status hyattn_linear_prefill_chunked_gated(hyattn_state_pool* pool, int linear_layer,
+                                                  const void* q, const void* k, const void* v,
+                                                  const float* log_gamma, void* o,
+                                                  const int32_t* cu_seqlens_dev,
+                                                  const int32_t* slots_dev, int n_req,
+                                                  int chunk_size, hyattn_dtype dtype,
+                                                  void* stream);
+hyattn_status hyattn_linear_decode_gated(hyattn_state_pool* pool, int linear_layer, const void* q,
+                                         const void* k, const void* v, const float* log_gamma,
+                                         void* o, const int32_t* slots_dev, int B,
+                                         hyattn_dtype dtype, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Full layers: paged KV cache of 16-token blocks (P2 §2.1 page table, P2 §2.3
  * PagedAttention decode, P1 §2.1 16 tokens per page).
@@ -200,6 +224,9 @@ typedef struct {
   void* o;       /* [N][H][D] */
   void* k_pool;  /* full layers: [n_blocks][H_kv][16][D]; linear: unused */
   void* v_pool;
+  const float* log_gamma; /* linear layers: NULL, or the gated variant's log forget
+                             factors fp32 [N][H] (prefill rows, then decode rows);
+                             full layers: must be NULL */
 } hyattn_layer_io;
 
 typedef struct {

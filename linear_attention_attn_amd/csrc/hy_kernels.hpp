@@ -11,13 +11,20 @@ namespace hy {
 hipError_t launch_state_zero(float* pool, int n_layers, int n_slots, int64_t slot_elems,
                              const int32_t* slots, int n, hipStream_t s);
 
+// log_gamma: NULL for the plain layer, else the gated variant's per-token log
+// forget factors, fp32 [N_tok][H] (decode: [B][H]).
 hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q, const void* k,
-                                const void* v, void* o, const int32_t* slots, int B, int H, int D,
-                                bool bf16, hipStream_t s);
+                                const void* v, void* o, const float* log_gamma,
+                                const int32_t* slots, int B, int H, int D, bool bf16,
+                                hipStream_t s);
 
 hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q, const void* k,
-                                 const void* v, void* o, const int32_t* cu, const int32_t* slots,
-                                 int n_req, int H, int D, int chunk, bool bf16, hipStream_t s);
+                                 const void* v, void* o, const float* log_gamma,
+                                 const int32_t* cu, const int32_t* slots, int n_req, int H, int D,
+                                 int chunk, bool bf16, hipStream_t s);
+
+// LDS bytes of the bf16 prefill kernel at chunk size C (plain or gated).
+size_t linear_prefill_bf16_lds_bytes(int D, int C, bool gated);
 
 // Largest chunk the fp32-I/O prefill kernel takes (its chunk scores live in LDS).
 constexpr int kMaxChunkF32 = 128;

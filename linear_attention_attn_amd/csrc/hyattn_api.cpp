@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -61,13 +62,14 @@ hyattn_status hip_status(hipError_t e, const char* what) {
 bool dtype_ok(hyattn_dtype dt) { return dt == HYATTN_F32 || dt == HYATTN_BF16; }
 bool d_ok(int D) { return D == 64 || D == 128; }
 
-// Copy a device int32 array to the host, synchronously on `s` (checked mode).
-hyattn_status fetch(std::vector<int32_t>& out, const int32_t* dev, size_t n, hipStream_t s) {
+// Copy a device array to the host, synchronously on `s` (checked mode).
+template <typename T>
+hyattn_status fetch(std::vector<T>& out, const T* dev, size_t n, hipStream_t s) {
   out.resize(n);
   if (n == 0) return ok();
-  hipError_t e = hipMemcpyAsync(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  hipError_t e = hipMemcpyAsync(out.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  return hip_status(e, "checked mode: reading index array");
+  return hip_status(e, "checked mode: reading an argument array");
 }
 
 hyattn_status check_slots(hyattn_state_pool* p, const int32_t* slots_dev, int n, hipStream_t s,
@@ -143,12 +145,22 @@ float* layer_base(const hyattn_state_pool* p, int layer) {
   return p->base + (size_t)layer * p->n_slots * p->H * (size_t)p->D * p->D;
 }
 
-bool prefill_chunk_ok(int D, int chunk, hyattn_dtype dt) {
+bool prefill_chunk_ok(int D, int chunk, hyattn_dtype dt, bool gated) {
   if (dt == HYATTN_F32) return chunk >= 1 && chunk <= hy::kMaxChunkF32;
   if (chunk < 16 || chunk > 256 || chunk % 16 != 0) return false;
-  const int Cp = (chunk + 31) & ~31;
-  const size_t lds = (size_t)(2 * Cp + 64) * D * 2;  // K, V tiles and the Q pair ring of the bf16 kernel
-  return lds <= 160 * 1024;
+  return hy::linear_prefill_bf16_lds_bytes(D, chunk, gated) <= 160 * 1024;
+}
+
+// Checked mode: the gated variant's log forget factors are finite and <= 0.
+hyattn_status check_log_gamma(const float* g_dev, size_t n, hipStream_t s) {
+  std::vector<float> g;
+  hyattn_status st = fetch(g, g_dev, n, s);
+  if (st != HYATTN_OK) return st;
+  for (size_t i = 0; i < n; ++i)
+    if (!(g[i] <= 0.f) || !std::isfinite(g[i]))
+      return fail(HYATTN_ERR_INVALID_ARG, "log_gamma[%zu] = %g is not a finite value <= 0", i,
+                  (double)g[i]);
+  return HYATTN_OK;
 }
 
 }  // namespace
@@ -157,7 +169,7 @@ extern "C" {
 
 const char* hyattn_last_error(void) { return g_err.c_str(); }
 
-int hyattn_abi_version(void) { return 1; }
+int hyattn_abi_version(void) { return 2; }
 
 // ---------------------------------------------------------------- state pool --
 size_t hyattn_state_pool_bytes(int n_linear_layers, int n_slots, int H, int D) {
@@ -281,22 +293,22 @@ void* hyattn_state_pool_state_ptr(const hyattn_state_pool* p, int layer, int slo
 }
 
 // ------------------------------------------------------------- linear layers --
-hyattn_status hyattn_linear_prefill_chunked(hyattn_state_pool* p, int layer, const void* q,
-                                            const void* k, const void* v, void* o,
-                                            const int32_t* cu_seqlens_dev,
-                                            const int32_t* slots_dev, int n_req, int chunk_size,
-                                            hyattn_dtype dtype, void* stream) {
+static hyattn_status linear_prefill(hyattn_state_pool* p, int layer, const void* q,
+                                    const void* k, const void* v, const float* log_gamma,
+                                    void* o, const int32_t* cu_seqlens_dev,
+                                    const int32_t* slots_dev, int n_req, int chunk_size,
+                                    hyattn_dtype dtype, void* stream, bool gated) {
   hyattn_status st = check_pool_layer(p, layer);
   if (st != HYATTN_OK) return st;
   if (!dtype_ok(dtype)) return fail(HYATTN_ERR_UNSUPPORTED, "dtype %d not supported", (int)dtype);
   if (n_req < 0) return fail(HYATTN_ERR_INVALID_ARG, "n_req = %d < 0", n_req);
-  if (!prefill_chunk_ok(p->D, chunk_size, dtype))
+  if (!prefill_chunk_ok(p->D, chunk_size, dtype, gated))
     return fail(HYATTN_ERR_UNSUPPORTED,
                 "chunk_size %d not supported (bf16: multiple of 16 in [16, 256] that fits LDS; "
                 "fp32: [1, %d])",
                 chunk_size, hy::kMaxChunkF32);
   if (n_req == 0) return ok();
-  if (!q || !k || !v || !o || !cu_seqlens_dev || !slots_dev)
+  if (!q || !k || !v || !o || !cu_seqlens_dev || !slots_dev || (gated && !log_gamma))
     return fail(HYATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
   hipStream_t s = as_stream(stream);
   if (checked_mode()) {
@@ -304,28 +316,69 @@ hyattn_status hyattn_linear_prefill_chunked(hyattn_state_pool* p, int layer, con
     if ((st = fetch(cu, cu_seqlens_dev, (size_t)n_req + 1, s)) != HYATTN_OK) return st;
     if ((st = check_cu(cu, -1, "cu_seqlens")) != HYATTN_OK) return st;
     if ((st = check_slots(p, slots_dev, n_req, s, true)) != HYATTN_OK) return st;
+    if (gated && (st = check_log_gamma(log_gamma, (size_t)cu[n_req] * p->H, s)) != HYATTN_OK)
+      return st;
   }
   return hip_status(hy::launch_linear_prefill(layer_base(p, layer), p->n_slots, q, k, v, o,
-                                              cu_seqlens_dev, slots_dev, n_req, p->H, p->D,
-                                              chunk_size, dtype == HYATTN_BF16, s),
+                                              gated ? log_gamma : nullptr, cu_seqlens_dev,
+                                              slots_dev, n_req, p->H, p->D, chunk_size,
+                                              dtype == HYATTN_BF16, s),
                     "linear prefill launch");
 }
 
-hyattn_status hyattn_linear_decode(hyattn_state_pool* p, int layer, const void* q, const void* k,
-                                   const void* v, void* o, const int32_t* slots_dev, int B,
-                                   hyattn_dtype dtype, void* stream) {
+static hyattn_status linear_decode(hyattn_state_pool* p, int layer, const void* q, const void* k,
+                                   const void* v, const float* log_gamma, void* o,
+                                   const int32_t* slots_dev, int B, hyattn_dtype dtype,
+                                   void* stream, bool gated) {
   hyattn_status st = check_pool_layer(p, layer);
   if (st != HYATTN_OK) return st;
   if (!dtype_ok(dtype)) return fail(HYATTN_ERR_UNSUPPORTED, "dtype %d not supported", (int)dtype);
   if (B < 0) return fail(HYATTN_ERR_INVALID_ARG, "B = %d < 0", B);
   if (B == 0) return ok();
-  if (!q || !k || !v || !o || !slots_dev)
+  if (!q || !k || !v || !o || !slots_dev || (gated && !log_gamma))
     return fail(HYATTN_ERR_INVALID_ARG, "a tensor pointer is NULL");
   hipStream_t s = as_stream(stream);
-  if (checked_mode() && (st = check_slots(p, slots_dev, B, s, true)) != HYATTN_OK) return st;
+  if (checked_mode()) {
+    if ((st = check_slots(p, slots_dev, B, s, true)) != HYATTN_OK) return st;
+    if (gated && (st = check_log_gamma(log_gamma, (size_t)B * p->H, s)) != HYATTN_OK) return st;
+  }
   return hip_status(hy::launch_linear_decode(layer_base(p, layer), p->n_slots, q, k, v, o,
-                                             slots_dev, B, p->H, p->D, dtype == HYATTN_BF16, s),
+                                             gated ? log_gamma : nullptr, slots_dev, B, p->H,
+                                             p->D, dtype == HYATTN_BF16, s),
                     "linear decode launch");
+}
+
+hyattn_status hyattn_linear_prefill_chunked(hyattn_state_pool* p, int layer, const void* q,
+                                            const void* k, const void* v, void* o,
+                                            const int32_t* cu_seqlens_dev,
+                                            const int32_t* slots_dev, int n_req, int chunk_size,
+                                            hyattn_dtype dtype, void* stream) {
+  return linear_prefill(p, layer, q, k, v, nullptr, o, cu_seqlens_dev, slots_dev, n_req,
+                        chunk_size, dtype, stream, false);
+}
+
+hyattn_status hyattn_linear_decode(hyattn_state_pool* p, int layer, const void* q, const void* k,
+                                   const void* v, void* o, const int32_t* slots_dev, int B,
+                                   hyattn_dtype dtype, void* stream) {
+  return linear_decode(p, layer, q, k, v, nullptr, o, slots_dev, B, dtype, stream, false);
+}
+
+hyattn_status hyattn_linear_prefill_chunked_gated(hyattn_state_pool* p, int layer, const void* q,
+                                                  const void* k, const void* v,
+                                                  const float* log_gamma, void* o,
+                                                  const int32_t* cu_seqlens_dev,
+                                                  const int32_t* slots_dev, int n_req,
+                                                  int chunk_size, hyattn_dtype dtype,
+                                                  void* stream) {
+  return linear_prefill(p, layer, q, k, v, log_gamma, o, cu_seqlens_dev, slots_dev, n_req,
+                        chunk_size, dtype, stream, true);
+}
+
+hyattn_status hyattn_linear_decode_gated(hyattn_state_pool* p, int layer, const void* q,
+                                         const void* k, const void* v, const float* log_gamma,
+                                         void* o, const int32_t* slots_dev, int B,
+                                         hyattn_dtype dtype, void* stream) {
+  return linear_decode(p, layer, q, k, v, log_gamma, o, slots_dev, B, dtype, stream, true);
 }
 
 // --------------------------------------------------------------- full layers --
@@ -556,7 +609,10 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
       return fail(HYATTN_ERR_INVALID_ARG, "prefill requests need cu_seqlens and slots");
     if (b->n_decode > 0 && !b->decode_slots)
       return fail(HYATTN_ERR_INVALID_ARG, "decode requests need slots");
-    if (b->n_prefill > 0 && !prefill_chunk_ok(b->D, b->chunk_size, b->dtype))
+    bool any_gated = false;
+    for (int i = 0; i < n_layers; ++i)
+      any_gated |= layer_types[i] == HYATTN_LAYER_LINEAR && layers[i].log_gamma != nullptr;
+    if (b->n_prefill > 0 && !prefill_chunk_ok(b->D, b->chunk_size, b->dtype, any_gated))
       return fail(HYATTN_ERR_UNSUPPORTED, "chunk_size %d not supported", b->chunk_size);
   }
   if (n_full > 0) {
@@ -577,6 +633,8 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
       return fail(HYATTN_ERR_INVALID_ARG, "layer %d: q/k/v/o pointer is NULL", i);
     if (layer_types[i] == HYATTN_LAYER_FULL && (!L.k_pool || !L.v_pool))
       return fail(HYATTN_ERR_INVALID_ARG, "layer %d: full layer without KV pools", i);
+    if (layer_types[i] == HYATTN_LAYER_FULL && L.log_gamma)
+      return fail(HYATTN_ERR_INVALID_ARG, "layer %d: log_gamma is for linear layers only", i);
   }
   if (getenv("HYATTN_LOG")) {
     std::string plan;
@@ -596,17 +654,20 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
   for (int i = 0; i < n_layers; ++i) {
     const hyattn_layer_io& L = layers[i];
     if (layer_types[i] == HYATTN_LAYER_LINEAR) {
+      const bool gated = L.log_gamma != nullptr;
       if (b->n_prefill > 0) {
-        st = hyattn_linear_prefill_chunked(p, li, L.q, L.k, L.v, L.o, b->cu_seqlens,
-                                           b->prefill_slots, b->n_prefill, b->chunk_size,
-                                           b->dtype, stream);
+        st = linear_prefill(p, li, L.q, L.k, L.v, L.log_gamma, L.o, b->cu_seqlens,
+                            b->prefill_slots, b->n_prefill, b->chunk_size, b->dtype, stream,
+                            gated);
         if (st != HYATTN_OK) return st;
       }
       if (b->n_decode > 0) {
         const size_t off = (size_t)n_prefill_tok * row_h;
-        st = hyattn_linear_decode(p, li, (const char*)L.q + off, (const char*)L.k + off,
-                                  (const char*)L.v + off, (char*)L.o + off, b->decode_slots,
-                                  b->n_decode, b->dtype, stream);
+        st = linear_decode(p, li, (const char*)L.q + off, (const char*)L.k + off,
+                           (const char*)L.v + off,
+                           gated ? L.log_gamma + (size_t)n_prefill_tok * b->H : nullptr,
+                           (char*)L.o + off, b->decode_slots, b->n_decode, b->dtype, stream,
+                           gated);
         if (st != HYATTN_OK) return st;
       }
       ++li;

@@ -14,6 +14,8 @@
 
 namespace hy {
 
+constexpr float kLog2e = 1.4426950408889634f;  // exp(x) = 2^(x log2 e)
+
 // ============================================================================
 // Zeroing: S[l][slot] = 0 for every linear layer l and listed slot.
 // grid (pieces, n, L); each block clears 64 KiB of one (layer, slot) region.
@@ -47,11 +49,12 @@ hipError_t launch_state_zero(float* pool, int n_layers, int n_slots, int64_t slo
 // accumulates q[i] S_new[i][j]. The per-thread partial outputs are summed over
 // the row groups in LDS in a fixed order (deterministic).
 // ============================================================================
-template <int D, typename T>
+template <int D, typename T, bool GATED>
 __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ states, int n_slots,
                                                        const T* __restrict__ q,
                                                        const T* __restrict__ k,
                                                        const T* __restrict__ v, T* __restrict__ o,
+                                                       const float* __restrict__ log_gamma,
                                                        const int32_t* __restrict__ slots, int H) {
   constexpr int C4 = D / 4;      // threads across a row (4 floats each)
   constexpr int RG = 256 / C4;   // row groups
@@ -82,11 +85,14 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
 
   const f32x4 vv = {sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float gamma = 1.f;
+  if constexpr (GATED) gamma = fast_exp2(log_gamma[unit] * kLog2e);
 #pragma unroll
   for (int j = 0; j < RP; ++j) {
     const int row = rg + RG * j;
     const float kr = sk[row], qr = sq[row];
     f32x4 x = s[j];
+    if constexpr (GATED) x *= gamma;  // S <- gamma S + k (x) v
     x[0] = __builtin_fmaf(kr, vv[0], x[0]);
     x[1] = __builtin_fmaf(kr, vv[1], x[1]);
     x[2] = __builtin_fmaf(kr, vv[2], x[2]);
@@ -111,18 +117,25 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
 }
 
 hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q, const void* k,
-                                const void* v, void* o, const int32_t* slots, int B, int H, int D,
-                                bool bf16, hipStream_t s) {
+                                const void* v, void* o, const float* log_gamma,
+                                const int32_t* slots, int B, int H, int D, bool bf16,
+                                hipStream_t s) {
   if (B <= 0) return hipSuccess;
   dim3 grid((unsigned)(B * H)), block(256);
-#define HY_DEC(DD, TT)                                                                        \
-  hipLaunchKernelGGL((k_linear_decode<DD, TT>), grid, block, 0, s, layer_states, n_slots,     \
-                     (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, slots, H)
+#define HY_DEC(DD, TT, GG)                                                                    \
+  hipLaunchKernelGGL((k_linear_decode<DD, TT, GG>), grid, block, 0, s, layer_states, n_slots, \
+                     (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, log_gamma, slots, H)
+#define HY_DEC_G(DD, TT)       \
+  if (log_gamma)               \
+    HY_DEC(DD, TT, true);      \
+  else                         \
+    HY_DEC(DD, TT, false)
   if (D == 128) {
-    if (bf16) HY_DEC(128, uint16_t); else HY_DEC(128, float);
+    if (bf16) HY_DEC_G(128, uint16_t); else HY_DEC_G(128, float);
   } else {
-    if (bf16) HY_DEC(64, uint16_t); else HY_DEC(64, float);
+    if (bf16) HY_DEC_G(64, uint16_t); else HY_DEC_G(64, float);
   }
+#undef HY_DEC_G
 #undef HY_DEC
   return hipGetLastError();
 }
@@ -134,19 +147,27 @@ hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q,
 //   o_a     = q_a . S + sum_b P[a][b] v_b
 //   S      += sum_b k_b (x) v_b
 // ============================================================================
-template <int D>
+//
+// Gated variant (GATED): token a of the chunk brings log forget factor g_a;
+// with L_a = g_0 + ... + g_a over the chunk (kept in LDS in log2 units),
+//   P[a][b] *= exp(L_a - L_b),  o_a = exp(L_a) q_a . S + sum_b P[a][b] v_b,
+//   S = exp(L_last) S + sum_b exp(L_last - L_b) k_b (x) v_b.
+template <int D, bool GATED>
 __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ states,
                                                             int n_slots,
                                                             const float* __restrict__ q,
                                                             const float* __restrict__ k,
                                                             const float* __restrict__ v,
                                                             float* __restrict__ o,
+                                                            const float* __restrict__ log_gamma,
                                                             const int32_t* __restrict__ cu,
                                                             const int32_t* __restrict__ slots,
                                                             int H, int C) {
   extern __shared__ __align__(16) float lds_f[];
   float* Ss = lds_f;          // D * D
   float* P = lds_f + D * D;   // C * C
+  float* Lc = P + C * C;      // C: L_a in log2 units (gated)
+  float* Wc = Lc + C;         // C: exp(L_last - L_b) (gated)
   const int unit = blockIdx.x;
   const int r = unit / H, h = unit - (unit / H) * H;
   const int tok0 = cu[r], T = cu[r + 1] - tok0;
@@ -163,6 +184,17 @@ __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ 
   __syncthreads();
   for (int c0 = 0; c0 < T; c0 += C) {
     const int n = (T - c0 < C) ? (T - c0) : C;
+    if constexpr (GATED) {
+      if (t == 0) {  // running sum in token order
+        float run = 0.f;
+        for (int a = 0; a < n; ++a) {
+          run += log_gamma[(int64_t)(tok0 + c0 + a) * H + h] * kLog2e;
+          Lc[a] = run;
+        }
+      }
+      __syncthreads();
+      for (int b = t; b < n; b += 256) Wc[b] = fast_exp2(Lc[n - 1] - Lc[b]);
+    }
     for (int idx = t; idx < n * n; idx += 256) {
       const int a = idx / n, b = idx - (idx / n) * n;
       float s = 0.f;
@@ -170,6 +202,7 @@ __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ 
         const float* qa = qb + (int64_t)(c0 + a) * ldx;
         const float* kk = kb + (int64_t)(c0 + b) * ldx;
         for (int i = 0; i < D; ++i) s = __builtin_fmaf(qa[i], kk[i], s);
+        if constexpr (GATED) s *= fast_exp2(Lc[a] - Lc[b]);
       }
       P[a * C + b] = s;
     }
@@ -179,16 +212,24 @@ __global__ __launch_bounds__(256) void k_linear_prefill_f32(float* __restrict__ 
       const float* qa = qb + (int64_t)(c0 + a) * ldx;
       float acc = 0.f;
       for (int i = 0; i < D; ++i) acc = __builtin_fmaf(qa[i], Ss[i * D + j], acc);
+      if constexpr (GATED) acc *= fast_exp2(Lc[a]);
       for (int b = 0; b <= a; ++b) acc = __builtin_fmaf(P[a * C + b], vb[(int64_t)(c0 + b) * ldx + j], acc);
       ob[(int64_t)(c0 + a) * ldx + j] = acc;
     }
     __syncthreads();
+    const float decay = GATED ? fast_exp2(Lc[n - 1]) : 1.f;
     for (int idx = t; idx < D * D; idx += 256) {
       const int i = idx / D, j = idx % D;
       float acc = 0.f;
-      for (int b = 0; b < n; ++b)
-        acc = __builtin_fmaf(kb[(int64_t)(c0 + b) * ldx + i], vb[(int64_t)(c0 + b) * ldx + j], acc);
-      Ss[idx] += acc;
+      for (int b = 0; b < n; ++b) {
+        float kw = kb[(int64_t)(c0 + b) * ldx + i];
+        if constexpr (GATED) kw *= Wc[b];
+        acc = __builtin_fmaf(kw, vb[(int64_t)(c0 + b) * ldx + j], acc);
+      }
+      if constexpr (GATED)
+        Ss[idx] = __builtin_fmaf(decay, Ss[idx], acc);
+      else
+        Ss[idx] += acc;
     }
     __syncthreads();
   }
@@ -284,17 +325,34 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   }
 }
 
-template <int D>
-size_t prefill_bf16_lds_bytes(int C) {
-  const int Cp = (C + 31) & ~31;
-  return (size_t)(2 * Cp + 2 * 32) * D * 2;  // K and V tiles of the chunk + Q pair ring
-}
+// Q ring slots: the gated kernel keeps one, so that its gate tables still
+// leave room for two workgroups per CU at C = 128 (80 KiB each).
+template <bool GATED>
+constexpr int prefill_q_slots() { return GATED ? 1 : 2; }
 
 template <int D>
+size_t prefill_bf16_lds_bytes(int C, bool gated) {
+  const int Cp = (C + 31) & ~31;
+  // K and V tiles of the chunk + Q pair ring (+ two per-token gate tables)
+  return gated ? (size_t)(2 * Cp + 32 * prefill_q_slots<true>()) * D * 2 + (size_t)2 * Cp * 4
+               : (size_t)(2 * Cp + 32 * prefill_q_slots<false>()) * D * 2;
+}
+
+// Gated variant (GATED): token a of the chunk brings log forget factor g_a
+// and L_a = g_0 + ... + g_a over the chunk, kept in LDS in log2 units (rows
+// past the chunk's end repeat the last value). Then
+//   O_c^T = exp(L_a) S^T q_a  (the inter-chunk part, scaled per query row)
+//         + V_c^T (tril(Q_c K_c^T) * exp(L_a - L_b))^T
+//   S     = exp(L_last) S + K_c^T diag(exp(L_last - L_b)) V_c
+// with the weighted V split into bf16 hi + lo, so the state stays
+// fp32-faithful. Wave 0 tabulates L and the state weights
+// W_b = exp2(L_last - L_b) once per chunk; each score takes one exp2.
+template <int D, bool GATED>
 __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     float* __restrict__ states, int n_slots, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int H, int C) {
+    const float* __restrict__ log_gamma, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ slots, int H, int C) {
   using Cfg = PrefillCfg<D>;
   constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = Cfg::CPR;
   extern __shared__ __align__(16) uint16_t lds_h[];
@@ -308,7 +366,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   const int Cp = (C + 31) & ~31;
   uint16_t* Ks = lds_h;
   uint16_t* Vs = Ks + Cp * D;
-  uint16_t* Qr = Vs + Cp * D;  // [2][32][D]: Q rows of the current and the next pair
+  constexpr int QS = prefill_q_slots<GATED>();
+  uint16_t* Qr = Vs + Cp * D;  // [QS][32][D]: Q rows of the current (and the next) pair
+  float* Lc = reinterpret_cast<float*>(Qr + QS * 32 * D);  // [Cp] L in log2 units (gated)
+  float* Wc = Lc + Cp;                                      // [Cp] W_b (gated)
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int dv0 = w * Cfg::DVW;
@@ -389,6 +450,35 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
         }
       }
     }
+    if constexpr (GATED) {
+      // L over the chunk: wave 0, four consecutive tokens per lane (Cp <= 256),
+      // then an inclusive scan of the lane totals across the wave
+      if (w == 0) {
+        float x[4], run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 4 * l + i;
+          run += (a < n) ? log_gamma[(int64_t)(tok0 + c0 + a) * H + h] * kLog2e : 0.f;
+          x[i] = run;
+        }
+        float incl = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(incl, off, 64);
+          if (l >= off) incl += y;
+        }
+        float excl = __shfl_up(incl, 1, 64);
+        if (l == 0) excl = 0.f;
+        const float last = __shfl(incl, 63, 64);  // L of the chunk's last token
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * l + i < Cp) {
+            const float la = excl + x[i];
+            Lc[4 * l + i] = la;
+            Wc[4 * l + i] = fast_exp2(last - la);
+          }
+      }
+    }
     __syncthreads();
 
     // ---- outputs, two 16-row tiles (32 query rows) at a time ----
@@ -399,8 +489,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     const int npr = (n + 31) >> 5;
     for (int j = 0; j < npr; ++j) {
       // the next pair: this chunk's j + 1, or the next chunk's first
-      if (j + 1 < npr) fetch_pair(c0, j + 1);
-      else fetch_pair(c0 + C, 0);
+      if constexpr (QS == 2) {
+        if (j + 1 < npr) fetch_pair(c0, j + 1);
+        else fetch_pair(c0 + C, 0);
+      }
       u32x4 qf[2][KS];
       {
         const uint16_t* src = Qr + pslot * 32 * D;
@@ -411,6 +503,14 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
             const int row = 16 * t2 + lr;
             qf[t2][s] = *reinterpret_cast<const u32x4*>(src + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
           }
+      }
+      if constexpr (QS == 1) {
+        // one slot: every wave holds its Q fragments before the slot is refilled
+        // at the end of this pair; the next pair's loads go out after the barrier
+        // (whose fence would otherwise wait for them)
+        __syncthreads();
+        if (j + 1 < npr) fetch_pair(c0, j + 1);
+        else fetch_pair(c0 + C, 0);
       }
 
       f32x4 Ot[2][NDV];
@@ -439,6 +539,16 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
           }
         }
       }
+      float lrow[2] = {0.f, 0.f};  // L of the lane's query row in each tile (gated)
+      if constexpr (GATED) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          lrow[t2] = Lc[32 * j + 16 * t2 + lr];
+          const float f = fast_exp2(lrow[t2]);
+#pragma unroll
+          for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] *= f;
+        }
+      }
 
       // intra-chunk: O^T += V^T P^T, P = tril(Q K^T), keys 0 .. 32 j + 31
       for (int kb32 = 0; kb32 <= j; ++kb32) {
@@ -461,6 +571,11 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
           }
         }
         u32x4 phi[2], plo[2];
+        f32x4 lkey[2];  // L of the lane's 8 keys (gated)
+        if constexpr (GATED) {
+          lkey[0] = *reinterpret_cast<const f32x4*>(Lc + 32 * kb32 + 8 * lg);
+          lkey[1] = *reinterpret_cast<const f32x4*>(Lc + 32 * kb32 + 8 * lg + 4);
+        }
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const int row = 32 * j + 16 * t2 + lr;
@@ -470,7 +585,9 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = 32 * kb32 + 8 * lg + 4 * u + i;
-              pv[4 * u + i] = (key <= row) ? pt[t2][u][i] : 0.f;
+              float p = pt[t2][u][i];
+              if constexpr (GATED) p *= fast_exp2(lrow[t2] - lkey[u][i]);
+              pv[4 * u + i] = (key <= row) ? p : 0.f;
             }
           split8(pv, phi[t2], plo[t2]);
         }
@@ -499,25 +616,63 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
           }
         }
       }
-      pslot ^= 1;
+      if constexpr (QS == 2) pslot ^= 1;
       store_pair(pslot);  // its previous readers finished before the last barrier
       __syncthreads();
     }
 
-    // ---- state update: S += K_c^T V_c ----
+    // ---- state update: S += K_c^T V_c (gated: S = exp(L_last) S + K_c^T W V_c) ----
     const int nts = (n + 31) >> 5;
-    for (int ts = 0; ts < nts; ++ts) {
-      const uint16_t* Kt = Ks + 32 * ts * D;
-      const uint16_t* Vt = Vs + 32 * ts * D;
-      u32x4 vf[NDV];
+    if constexpr (GATED) {
+      const float last = Lc[Cp - 1];
+      const float decay = fast_exp2(last);
 #pragma unroll
-      for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+      for (int t = 0; t < NDK; ++t)
 #pragma unroll
-      for (int t = 0; t < NDK; ++t) {
-        // A operand: K^T rows pi(t, m) = columns of the K tile
-        const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
+        for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] *= decay;
+      for (int ts = 0; ts < nts; ++ts) {
+        const uint16_t* Kt = Ks + 32 * ts * D;
+        const uint16_t* Vt = Vs + 32 * ts * D;
+        // the lane's V operand holds tokens 32 ts + 8 (l / 16) + 0..7
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wc + 32 * ts + 8 * lg);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wc + 32 * ts + 8 * lg + 4);
+        const float wt[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        u32x4 vhi[NDV], vlo[NDV];
 #pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt, vf[nn], Sacc[t][nn]);
+        for (int nn = 0; nn < NDV; ++nn) {
+          const u32x4 vf = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+          float x[8];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            x[2 * p] = bf16_lo(vf[p]) * wt[2 * p];
+            x[2 * p + 1] = bf16_hi(vf[p]) * wt[2 * p + 1];
+          }
+          split8(x, vhi[nn], vlo[nn]);
+        }
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+          const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
+#pragma unroll
+          for (int nn = 0; nn < NDV; ++nn) {
+            Sacc[t][nn] = mfma16x16x32(kt, vhi[nn], Sacc[t][nn]);
+            Sacc[t][nn] = mfma16x16x32(kt, vlo[nn], Sacc[t][nn]);
+          }
+        }
+      }
+    } else {
+      for (int ts = 0; ts < nts; ++ts) {
+        const uint16_t* Kt = Ks + 32 * ts * D;
+        const uint16_t* Vt = Vs + 32 * ts * D;
+        u32x4 vf[NDV];
+#pragma unroll
+        for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+          // A operand: K^T rows pi(t, m) = columns of the K tile
+          const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
+#pragma unroll
+          for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt, vf[nn], Sacc[t][nn]);
+        }
       }
     }
   }
@@ -531,6 +686,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
         S[(int64_t)state_row(t, 4 * lg + i) * D + dv0 + 16 * n + lr] = Sacc[t][n][i];
 }
 
+size_t linear_prefill_bf16_lds_bytes(int D, int C, bool gated) {
+  return D == 128 ? prefill_bf16_lds_bytes<128>(C, gated) : prefill_bf16_lds_bytes<64>(C, gated);
+}
+
 template <typename K>
 static hipError_t allow_lds(K kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
@@ -539,39 +698,43 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
 }
 
 hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q, const void* k,
-                                 const void* v, void* o, const int32_t* cu, const int32_t* slots,
-                                 int n_req, int H, int D, int chunk, bool bf16, hipStream_t s) {
+                                 const void* v, void* o, const float* log_gamma,
+                                 const int32_t* cu, const int32_t* slots, int n_req, int H, int D,
+                                 int chunk, bool bf16, hipStream_t s) {
   if (n_req <= 0) return hipSuccess;
   dim3 grid((unsigned)(n_req * H)), block(256);
+  const bool gated = log_gamma != nullptr;
   hipError_t e;
   if (bf16) {
-#define HY_LP(DD)                                                                              \
+#define HY_LP(DD, GG)                                                                          \
   do {                                                                                         \
-    const size_t lds = prefill_bf16_lds_bytes<DD>(chunk);                                      \
-    if ((e = allow_lds(k_linear_prefill_bf16<DD>, lds)) != hipSuccess) return e;               \
-    hipLaunchKernelGGL((k_linear_prefill_bf16<DD>), grid, block, lds, s, layer_states, n_slots, \
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, \
-                       cu, slots, H, chunk);                                                   \
+    const size_t lds = prefill_bf16_lds_bytes<DD>(chunk, GG);                                  \
+    if ((e = allow_lds(k_linear_prefill_bf16<DD, GG>, lds)) != hipSuccess) return e;           \
+    hipLaunchKernelGGL((k_linear_prefill_bf16<DD, GG>), grid, block, lds, s, layer_states,     \
+                       n_slots, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,    \
+                       (uint16_t*)o, log_gamma, cu, slots, H, chunk);                          \
   } while (0)
     if (D == 128) {
-      HY_LP(128);
+      if (gated) HY_LP(128, true); else HY_LP(128, false);
     } else {
-      HY_LP(64);
+      if (gated) HY_LP(64, true); else HY_LP(64, false);
     }
 #undef HY_LP
   } else {
-    const size_t lds = (size_t)(D * D + chunk * chunk) * sizeof(float);
+    const size_t lds = (size_t)(D * D + chunk * chunk + (gated ? 2 * chunk : 0)) * sizeof(float);
+#define HY_LPF(DD, GG)                                                                           \
+  do {                                                                                           \
+    if ((e = allow_lds(k_linear_prefill_f32<DD, GG>, lds)) != hipSuccess) return e;              \
+    hipLaunchKernelGGL((k_linear_prefill_f32<DD, GG>), grid, block, lds, s, layer_states,        \
+                       n_slots, (const float*)q, (const float*)k, (const float*)v, (float*)o,    \
+                       log_gamma, cu, slots, H, chunk);                                          \
+  } while (0)
     if (D == 128) {
-      if ((e = allow_lds(k_linear_prefill_f32<128>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_linear_prefill_f32<128>, grid, block, lds, s, layer_states, n_slots,
-                         (const float*)q, (const float*)k, (const float*)v, (float*)o, cu, slots,
-                         H, chunk);
+      if (gated) HY_LPF(128, true); else HY_LPF(128, false);
     } else {
-      if ((e = allow_lds(k_linear_prefill_f32<64>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(k_linear_prefill_f32<64>, grid, block, lds, s, layer_states, n_slots,
-                         (const float*)q, (const float*)k, (const float*)v, (float*)o, cu, slots,
-                         H, chunk);
+      if (gated) HY_LPF(64, true); else HY_LPF(64, false);
     }
+#undef HY_LPF
   }
   return hipGetLastError();
 }

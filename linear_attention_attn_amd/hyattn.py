@@ -33,6 +33,7 @@ EXPORTS = (
     "hyattn_paged_append", "hyattn_paged_decode_workspace_bytes", "hyattn_paged_decode",
     "hyattn_paged_prefill", "hyattn_hybrid_workspace_bytes", "hyattn_hybrid_step",
     "hyattn_estimate_memory",
+    "hyattn_linear_prefill_chunked_gated", "hyattn_linear_decode_gated",
     "hyattn_bucket_by_length",
 )
 
@@ -46,7 +47,7 @@ class HyattnError(RuntimeError):
 
 class LayerIO(C.Structure):
     _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p), ("o", C.c_void_p),
-                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p)]
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("log_gamma", C.c_void_p)]
 
 
 class Batch(C.Structure):
@@ -68,6 +69,7 @@ class MemoryEstimate(C.Structure):
 
 
 _lib = None
+ABI_VERSION = 2  # must match hyattn_abi_version() of the loaded library
 
 
 def lib_path() -> str:
@@ -98,6 +100,9 @@ def load():
         "hyattn_state_pool_state_ptr": ([vp, i, i], vp),
         "hyattn_linear_prefill_chunked": ([vp, i, vp, vp, vp, vp, vp, vp, i, i, i, vp], st),
         "hyattn_linear_decode": ([vp, i, vp, vp, vp, vp, vp, i, i, vp], st),
+        "hyattn_linear_prefill_chunked_gated": ([vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, vp],
+                                                st),
+        "hyattn_linear_decode_gated": ([vp, i, vp, vp, vp, vp, vp, vp, i, i, vp], st),
         "hyattn_paged_append": ([vp, vp, vp, vp, i64, vp, i, vp, vp, i, i, i, i, i, vp], st),
         "hyattn_paged_decode_workspace_bytes": ([i, i, i, i], sz),
         "hyattn_paged_decode": ([vp, vp, vp, vp, i64, vp, i, vp, i, i, i, i, i, f, vp, sz, i,
@@ -113,6 +118,9 @@ def load():
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = res
+    if L.hyattn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH}: ABI version {L.hyattn_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}; rebuild the library")
     _lib = L
     return L
 
@@ -210,6 +218,21 @@ def hyattn_linear_prefill_chunked(pool, linear_layer, q, k, v, o, cu_seqlens, sl
 def hyattn_linear_decode(pool, linear_layer, q, k, v, o, slots, B, dtype, stream=None):
     _check(load().hyattn_linear_decode(pool, linear_layer, ptr(q), ptr(k), ptr(v), ptr(o),
                                        ptr(slots), B, dtype, _stream(stream)))
+
+
+def hyattn_linear_prefill_chunked_gated(pool, linear_layer, q, k, v, log_gamma, o, cu_seqlens,
+                                        slots, n_req, chunk_size, dtype, stream=None):
+    _check(load().hyattn_linear_prefill_chunked_gated(pool, linear_layer, ptr(q), ptr(k), ptr(v),
+                                                      ptr(log_gamma), ptr(o), ptr(cu_seqlens),
+                                                      ptr(slots), n_req, chunk_size, dtype,
+                                                      _stream(stream)))
+
+
+def hyattn_linear_decode_gated(pool, linear_layer, q, k, v, log_gamma, o, slots, B, dtype,
+                               stream=None):
+    _check(load().hyattn_linear_decode_gated(pool, linear_layer, ptr(q), ptr(k), ptr(v),
+                                             ptr(log_gamma), ptr(o), ptr(slots), B, dtype,
+                                             _stream(stream)))
 
 
 def hyattn_paged_append(k_new, v_new, k_pool, v_pool, n_blocks, block_tables, max_blocks_per_seq,

@@ -184,3 +184,15 @@ WORKLOADS = {
                         n_decode=240, ctx_lo=512, ctx_hi=131072, chunk=128,
                         dtype="bf16"),
 }
+
+
+def device_log_forget(shape, seed: int, device="cuda"):
+    """log_forget's distribution drawn on the device (float32 [N][H]): head h
+    takes gamma = 1 - u * 2^-(2 + h % 8), u ~ U(0, 1)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    N, H = shape
+    u = torch.rand((N, H), generator=g, device=device, dtype=torch.float64)
+    e = 2.0 + (torch.arange(H, device=device, dtype=torch.float64) % 8)
+    return torch.log1p(-u * torch.exp2(-e)).clamp(max=0.0).to(torch.float32)

@@ -38,6 +38,8 @@ def run_gpu(case, slot_perm=None):
     for t, io in zip(types, case["layers"]):
         d = {n: gu.dev(io[n]) for n in ("q", "k", "v")}
         d["o"] = torch.full_like(d["q"], float("nan"))
+        if "g" in io:  # gated linear layer
+            d["log_gamma"] = gu.dev(io["g"])
         if t == 1:
             d["k_pool"], d["v_pool"] = (gu.dev(x) for x in case["pools"][fi])
             fi += 1
@@ -149,6 +151,8 @@ def run_gpu_steps(case):
         for t, io in zip(types, case["layers"]):
             d = {n: gu.dev(io[n][order]) for n in ("q", "k", "v")}
             d["o"] = torch.full_like(d["q"], float("nan"))
+            if "g" in io:  # gated linear layer
+                d["log_gamma"] = gu.dev(io["g"][order])
             if t == 1:
                 d["k_pool"], d["v_pool"] = dev_pools[fi]
                 fi += 1

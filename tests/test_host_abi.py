@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(hy.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert hy.hyattn_abi_version() == 1
+    assert hy.hyattn_abi_version() == hy.ABI_VERSION == 2
 
 
 def test_library_is_gfx950_code_object():
