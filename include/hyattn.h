@@ -126,7 +126,11 @@ void* hyattn_state_pool_state_ptr(const hyattn_state_pool* pool, int linear_laye
  *   chunk_size   tokens per chunk: a multiple of 16 in [16, 256] (bf16);
  *                in [1, 128] for fp32 I/O. For each chunk c (the last may be
  *                shorter): O_c = Q_c S + tril(Q_c K_c^T) V_c, then
- *                S <- S + K_c^T V_c.
+ *                S <- S + K_c^T V_c. Every chunking gives the same sums
+ *                (P2 §2.4), so results differ between chunk sizes by
+ *                rounding only; the bf16 kernel always works in 32-token
+ *                blocks (streamed through LDS), the fp32 kernel in chunks of
+ *                chunk_size.
  * Requests with zero tokens are left untouched. */
 hyattn_status hyattn_linear_prefill_chunked(hyattn_state_pool* pool, int linear_layer,
                                             const void* q, const void* k, const void* v, void* o,

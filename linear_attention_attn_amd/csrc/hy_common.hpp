@@ -87,15 +87,17 @@ __device__ __forceinline__ u32x2 ds_read_tr16_raw(const uint16_t* lds) {
 // registers passed in are tied to the wait so no use of them moves above it.
 template <int N>
 __device__ __forceinline__ void lds_wait_all(u32x4 (&x)[N]) {
-  static_assert(N == 8 || N == 4 || N == 2, "lds_wait_all: 2, 4 or 8 fragments");
+  static_assert(N == 8 || N == 4 || N == 2 || N == 1, "lds_wait_all: 1, 2, 4 or 8 fragments");
   if constexpr (N == 8)
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
                    "+v"(x[6]), "+v"(x[7]));
   else if constexpr (N == 4)
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
-  else
+  else if constexpr (N == 2)
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]));
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]));
 }
 
 // 8 consecutive rows row0 + 8*(l/16) + 0..7 of column col_q(l%16 / 4) + l%4 of
@@ -118,6 +120,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Workgroup barrier for LDS hand-offs only: waits for the wave's own LDS
+// operations, then s_barrier. Unlike __syncthreads it has no release fence,
+// so global stores and loads still in flight (outputs on their way to HBM,
+// the next tile's prefetch) are not drained at every barrier. Only for
+// kernels whose waves share data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left at their maxima): vmcnt is split over

@@ -325,36 +325,77 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   }
 }
 
-// Q ring slots: the gated kernel keeps one, so that its gate tables still
-// leave room for two workgroups per CU at C = 128 (80 KiB each).
-template <bool GATED>
-constexpr int prefill_q_slots() { return GATED ? 1 : 2; }
-
-template <int D>
-size_t prefill_bf16_lds_bytes(int C, bool gated) {
-  const int Cp = (C + 31) & ~31;
-  // K and V tiles of the chunk + Q pair ring (+ two per-token gate tables)
-  return gated ? (size_t)(2 * Cp + 32 * prefill_q_slots<true>()) * D * 2 + (size_t)2 * Cp * 4
-               : (size_t)(2 * Cp + 32 * prefill_q_slots<false>()) * D * 2;
+// Raw transposing read of the same operand (see ds_read_tr16_raw): for loops
+// that keep global-to-LDS loads in flight. Wait with lds_wait_all before use.
+template <int D, bool IS_K>
+__device__ __forceinline__ u32x4 tr_swz_raw(const uint16_t* tile, int col_src) {
+  const int l = threadIdx.x & 63;
+  const int row = 8 * (l >> 4) + ((l & 15) >> 2);
+  const uint16_t* p = tile + swz_off<D>(row, col_src, IS_K ? kswz<D>(row) : vswz<D>(row));
+  const u32x2 a = ds_read_tr16_raw(p);
+  const u32x2 b = ds_read_tr16_raw(p + 4 * D);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// Gated variant (GATED): token a of the chunk brings log forget factor g_a
-// and L_a = g_0 + ... + g_a over the chunk, kept in LDS in log2 units (rows
-// past the chunk's end repeat the last value). Then
-//   O_c^T = exp(L_a) S^T q_a  (the inter-chunk part, scaled per query row)
-//         + V_c^T (tril(Q_c K_c^T) * exp(L_a - L_b))^T
-//   S     = exp(L_last) S + K_c^T diag(exp(L_last - L_b)) V_c
-// with the weighted V split into bf16 hi + lo, so the state stays
-// fp32-faithful. Wave 0 tabulates L and the state weights
-// W_b = exp2(L_last - L_b) once per chunk; each score takes one exp2.
+// Token blocks of the bf16 prefill: 32 tokens, i.e. one pair of 16-row MFMA
+// tiles. The state is brought up to date after every block, so a block's
+// output needs the causal scores of the block itself only.
+constexpr int kLinBlock = 32;
+// LDS ring of token blocks (K, V and Q tiles of 32 x D each, + gates)
+constexpr int kLinRing = 3;
+
+template <int D, bool GATED>
+struct LinRing {
+  static constexpr int TILE = kLinBlock * D;              // elements of one tile
+  static constexpr int GATE = GATED ? 4 * 64 * 2 : 0;     // 4 waves x 64 fp32 (as bf16 units)
+  static constexpr int SLOT = 3 * TILE + GATE;            // elements (uint16) per slot
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;                    // rows per 1 KiB load instruction
+  static constexpr int IPT = kLinBlock / RPI;             // load instructions per tile
+  static constexpr int IPB = 3 * IPT / 4;                 // tile loads per wave per block
+  static constexpr int VMB = IPB + (GATED ? 1 : 0);       // vector-memory loads per wave per block
+  static_assert(3 * IPT % 4 == 0, "tile loads split evenly over 4 waves");
+};
+
+template <int D>
+size_t prefill_bf16_lds_bytes(int /*C*/, bool gated) {
+  return gated ? (size_t)kLinRing * LinRing<D, true>::SLOT * 2
+               : (size_t)kLinRing * LinRing<D, false>::SLOT * 2;
+}
+
+// Chunked prefill, streaming form. One workgroup (4 waves) per (request,
+// head); wave w keeps value columns [w D/4, (w+1) D/4) of the fp32 state in
+// accumulator registers for the whole request. The request's tokens pass in
+// 32-token blocks; K, V and Q of block b move from HBM straight into a
+// 3-slot LDS ring (global_load_lds, no registers hold the data in flight),
+// requested two blocks ahead of their use, with each lane's 16-byte load
+// aimed so that the tiles land XOR-swizzled per row. Per block, each wave
+// computes for its value columns
+//   O_b^T = S^T Q_b^T               (S split into bf16 hi + lo: fp32-faithful)
+//         + V_b^T tril(Q_b K_b^T)^T (scores in fp32, split hi + lo likewise)
+//   S    += K_b^T V_b
+// which is the chunk form of P2 §2.4 with 32-token chunks: any chunking gives
+// the same sums, so the caller's chunk size only fixes the reference it is
+// compared against. One barrier per block, with no release fence: output
+// stores stay in flight across it; transposing reads are issued as opaque
+// instructions so that the compiler does not drain the ring's loads before
+// them.
+// Gated variant (GATED): the block's 32 log forget factors travel with the
+// tiles (each wave loads its own copy); a 32-lane scan gives L_a = g_0 + ..
+// + g_a over the block, and
+//   O_b^T = exp(L_a) S^T q_a + V_b^T (tril(Q_b K_b^T) * exp(L_a - L_c))^T
+//   S     = exp(L_last) S + K_b^T diag(exp(L_last - L_c)) V_b
+// with the weighted V split hi + lo.
 template <int D, bool GATED>
 __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     float* __restrict__ states, int n_slots, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
     const float* __restrict__ log_gamma, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ slots, int H, int C) {
+    const int32_t* __restrict__ slots, int H, int /*C*/) {
   using Cfg = PrefillCfg<D>;
-  constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = Cfg::CPR;
+  using R = LinRing<D, GATED>;
+  constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = R::CPR, RPI = R::RPI;
+  constexpr int TILE = R::TILE, IPT = R::IPT, IPB = R::IPB, VMB = R::VMB;
   extern __shared__ __align__(16) uint16_t lds_h[];
 
   const int unit = blockIdx.x;
@@ -362,14 +403,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   const int tok0 = cu[r], T = cu[r + 1] - tok0;
   const int slot = slots[r];
   if (T <= 0 || slot < 0 || slot >= n_slots) return;
-
-  const int Cp = (C + 31) & ~31;
-  uint16_t* Ks = lds_h;
-  uint16_t* Vs = Ks + Cp * D;
-  constexpr int QS = prefill_q_slots<GATED>();
-  uint16_t* Qr = Vs + Cp * D;  // [QS][32][D]: Q rows of the current (and the next) pair
-  float* Lc = reinterpret_cast<float*>(Qr + QS * 32 * D);  // [Cp] L in log2 units (gated)
-  float* Wc = Lc + Cp;                                      // [Cp] W_b (gated)
+  const int nb = (T + kLinBlock - 1) / kLinBlock;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int dv0 = w * Cfg::DVW;
@@ -380,6 +414,44 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   const uint16_t* vb = v + (int64_t)tok0 * ldx + (int64_t)h * D;
   uint16_t* ob = o + (int64_t)tok0 * ldx + (int64_t)h * D;
 
+  // ---- block loads: wave w moves pieces w IPB .. w IPB + IPB - 1 of the
+  // block's 3 IPT pieces (K pieces, then V, then Q; RPI rows each). Rows past
+  // the request's end load its last token (finite data; V rows are cleared
+  // before use, K and Q rows only meet masked scores or unstored outputs).
+  auto issue = [&](int b, int sl) {
+    uint16_t* base = lds_h + sl * R::SLOT;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int ig = w * IPB + i;
+      const int tensor = ig / IPT, piece = ig - (ig / IPT) * IPT;
+      const int row = piece * RPI + l / CPR;
+      const int tok = min(kLinBlock * b + row, T - 1);
+      const int x = tensor == 0 ? kswz<D>(row) : (tensor == 1 ? vswz<D>(row) : qswz<D>(row));
+      const uint16_t* src = (tensor == 0 ? kb : (tensor == 1 ? vb : qb)) + (int64_t)tok * ldx +
+                            8 * ((l % CPR) ^ x);
+      uint16_t* dst = base + tensor * TILE + piece * RPI * D;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    if constexpr (GATED) {  // this wave's copy of the block's forget factors (lanes 32..63 repeat)
+      const int tok = min(kLinBlock * b + (l & 31), T - 1);
+      const float* src = log_gamma + (int64_t)(tok0 + tok) * H + h;
+      uint16_t* dst = base + 3 * TILE + w * 128;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+  };
+  // V rows past the request's end, among this wave's pieces, become zeros
+  auto clear_tail = [&](int sl, int n) {
+    uint16_t* base = lds_h + sl * R::SLOT;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int ig = w * IPB + i;
+      const int tensor = ig / IPT, piece = ig - (ig / IPT) * IPT;
+      const int row = piece * RPI + l / CPR;
+      if (tensor == 1 && row >= n)
+        *reinterpret_cast<u32x4*>(base + TILE + piece * RPI * D + 8 * l) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
   f32x4 Sacc[NDK][NDV];
 #pragma unroll
   for (int t = 0; t < NDK; ++t)
@@ -389,291 +461,183 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
       for (int i = 0; i < 4; ++i)
         Sacc[t][n][i] = S[(int64_t)state_row(t, 4 * lg + i) * D + dv0 + 16 * n + lr];
 
-  // ---- Q pairs (32 query rows) stream through a 2-deep LDS ring ----
-  // Pair p of the request (chunk c0 = C * (p / pairs per chunk)) sits in
-  // slot p % 2. Its rows are fetched by the whole workgroup one pair ahead
-  // (two 16-byte loads per thread) and stored after the current pair's
-  // compute, behind the barrier that closes it.
-  constexpr int QPT = 32 * CPR / 256;  // 16-byte pieces per thread per pair
-  const int qc = tid % CPR, qr0 = tid / CPR;
-  u32x4 qst[QPT];
-  const int ppc = (C + 31) >> 5;  // pairs per full chunk
-  auto fetch_pair = [&](int cc0, int jj) {  // rows 32 jj .. of the chunk at cc0 (zero past T)
-    const int nn_ = (T - cc0 < C) ? (T - cc0) : C;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int a = 32 * jj + qr0 + (256 / CPR) * i;
-      qst[i] = (cc0 < T && a < nn_) ? *reinterpret_cast<const u32x4*>(qb + (int64_t)(cc0 + a) * ldx + 8 * qc)
-                                   : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_pair = [&](int slot) {
-    uint16_t* dst = Qr + slot * 32 * D;
-#pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int a = qr0 + (256 / CPR) * i;
-      *reinterpret_cast<u32x4*>(dst + swz_off<D>(a, 8 * qc, qswz<D>(a))) = qst[i];
-    }
-  };
-  int pslot = 0;  // ring slot of the current pair
-  fetch_pair(0, 0);
-  store_pair(0);  // made visible by the first staging barrier below
+  for (int i = 0; i < kLinRing - 1; ++i)
+    if (i < nb) issue(i, i);
 
-  for (int c0 = 0; c0 < T; c0 += C) {
-    const int n = (T - c0 < C) ? (T - c0) : C;
-    __syncthreads();  // the previous chunk's tiles are no longer read
-    // ---- stage K and V (rows past n are zero) ----
-    {
-      constexpr int TGS = 256 / CPR;    // 4-token groups per pass
-      const int dk8 = tid % CPR, tg = tid / CPR;
-      for (int slab = 0; slab < Cp; slab += 4 * TGS) {
-        const int a0 = slab + 4 * tg;
-        if (a0 >= Cp) continue;
-        u32x4 rk[4], rv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int a = a0 + i;
-          if (a < n) {
-            const int64_t off = (int64_t)(c0 + a) * ldx + 8 * dk8;
-            rk[i] = *reinterpret_cast<const u32x4*>(kb + off);
-            rv[i] = *reinterpret_cast<const u32x4*>(vb + off);
-          } else {
-            rk[i] = u32x4{0u, 0u, 0u, 0u};
-            rv[i] = rk[i];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int a = a0 + i;
-          *reinterpret_cast<u32x4*>(Ks + swz_off<D>(a, 8 * dk8, kswz<D>(a))) = rk[i];
-          *reinterpret_cast<u32x4*>(Vs + swz_off<D>(a, 8 * dk8, vswz<D>(a))) = rv[i];
-        }
-      }
-    }
-    if constexpr (GATED) {
-      // L over the chunk: wave 0, four consecutive tokens per lane (Cp <= 256),
-      // then an inclusive scan of the lane totals across the wave
-      if (w == 0) {
-        float x[4], run = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int a = 4 * l + i;
-          run += (a < n) ? log_gamma[(int64_t)(tok0 + c0 + a) * H + h] * kLog2e : 0.f;
-          x[i] = run;
-        }
-        float incl = run;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(incl, off, 64);
-          if (l >= off) incl += y;
-        }
-        float excl = __shfl_up(incl, 1, 64);
-        if (l == 0) excl = 0.f;
-        const float last = __shfl(incl, 63, 64);  // L of the chunk's last token
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * l + i < Cp) {
-            const float la = excl + x[i];
-            Lc[4 * l + i] = la;
-            Wc[4 * l + i] = fast_exp2(last - la);
-          }
-      }
-    }
-    __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    const int sl = b % kLinRing;
+    const int n = min(kLinBlock, T - kLinBlock * b);
+    // this wave's loads of block b have landed (block b + 1's may still fly)
+    if (b + 1 < nb) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (n < kLinBlock) clear_tail(sl, n);
+    lds_barrier();  // block b visible to all waves; block b - 1's slot is free
+    if (b + kLinRing - 1 < nb) issue(b + kLinRing - 1, (b + kLinRing - 1) % kLinRing);
 
-    // ---- outputs, two 16-row tiles (32 query rows) at a time ----
-    // Both tiles of a pair see the same key blocks, so every K and V
-    // fragment read from LDS feeds two tiles, and the pair gives 4 to 8
-    // independent accumulator chains. The pair's Q fragments arrive one pair
-    // ahead of their use.
-    const int npr = (n + 31) >> 5;
-    for (int j = 0; j < npr; ++j) {
-      // the next pair: this chunk's j + 1, or the next chunk's first
-      if constexpr (QS == 2) {
-        if (j + 1 < npr) fetch_pair(c0, j + 1);
-        else fetch_pair(c0 + C, 0);
-      }
-      u32x4 qf[2][KS];
-      {
-        const uint16_t* src = Qr + pslot * 32 * D;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            const int row = 16 * t2 + lr;
-            qf[t2][s] = *reinterpret_cast<const u32x4*>(src + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
-          }
-      }
-      if constexpr (QS == 1) {
-        // one slot: every wave holds its Q fragments before the slot is refilled
-        // at the end of this pair; the next pair's loads go out after the barrier
-        // (whose fence would otherwise wait for them)
-        __syncthreads();
-        if (j + 1 < npr) fetch_pair(c0, j + 1);
-        else fetch_pair(c0 + C, 0);
-      }
+    const uint16_t* Kt = lds_h + sl * R::SLOT;
+    const uint16_t* Vt = Kt + TILE;
+    const uint16_t* Qt = Vt + TILE;
 
-      f32x4 Ot[2][NDV];
+    u32x4 qf[2][KS];
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      // inter-chunk: O^T += S^T Q^T with the state before this chunk
+    for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) {
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = Sacc[2 * s][nn][i];
-            x[4 + i] = Sacc[2 * s + 1][nn][i];
-          }
-          u32x4 shi, slo;
-          split8(x, shi, slo);
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            Ot[t2][nn] = mfma16x16x32(shi, qf[t2][s], Ot[t2][nn]);
-            Ot[t2][nn] = mfma16x16x32(slo, qf[t2][s], Ot[t2][nn]);
-          }
-        }
-      }
-      float lrow[2] = {0.f, 0.f};  // L of the lane's query row in each tile (gated)
-      if constexpr (GATED) {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          lrow[t2] = Lc[32 * j + 16 * t2 + lr];
-          const float f = fast_exp2(lrow[t2]);
-#pragma unroll
-          for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] *= f;
-        }
+        const int row = 16 * t2 + lr;
+        qf[t2][s] = *reinterpret_cast<const u32x4*>(Qt + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
       }
 
-      // intra-chunk: O^T += V^T P^T, P = tril(Q K^T), keys 0 .. 32 j + 31
-      for (int kb32 = 0; kb32 <= j; ++kb32) {
-        const uint16_t* Kt = Ks + 32 * kb32 * D;
-        const uint16_t* Vt = Vs + 32 * kb32 * D;
-        f32x4 pt[2][2];
+    // gated: L of the lane's query rows and keys, and of the block's last token
+    float lrow[2] = {0.f, 0.f}, lkey[8], last = 0.f;
+    if constexpr (GATED) {
+      const float* gw = reinterpret_cast<const float*>(Qt + TILE) + w * 64;
+      float x = ((l & 31) < n) ? gw[l & 31] * kLog2e : 0.f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) pt[t2][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
-#pragma unroll
-          for (int s = 0; s < KS; ++s) {
-            const u32x4 kf =
-                *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 32 * s + 8 * lg, kswz<D>(krow)));
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) pt[t2][u] = mfma16x16x32(kf, qf[t2][s], pt[t2][u]);
-          }
-        }
-        u32x4 phi[2], plo[2];
-        f32x4 lkey[2];  // L of the lane's 8 keys (gated)
-        if constexpr (GATED) {
-          lkey[0] = *reinterpret_cast<const f32x4*>(Lc + 32 * kb32 + 8 * lg);
-          lkey[1] = *reinterpret_cast<const f32x4*>(Lc + 32 * kb32 + 8 * lg + 4);
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int row = 32 * j + 16 * t2 + lr;
-          float pv[8];
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = 32 * kb32 + 8 * lg + 4 * u + i;
-              float p = pt[t2][u][i];
-              if constexpr (GATED) p *= fast_exp2(lrow[t2] - lkey[u][i]);
-              pv[4 * u + i] = (key <= row) ? p : 0.f;
-            }
-          split8(pv, phi[t2], plo[t2]);
-        }
-#pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) {
-          const u32x4 vf = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            Ot[t2][nn] = mfma16x16x32(vf, phi[t2], Ot[t2][nn]);
-            Ot[t2][nn] = mfma16x16x32(vf, plo[t2], Ot[t2][nn]);
-          }
-        }
+      for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(x, off, 32);
+        if ((l & 31) >= off) x += y;
       }
-
-      // lane holds O^T[value col 16 nn + 4 lg + i][query row lr] of each tile
+      lrow[0] = __shfl(x, lr, 64);
+      lrow[1] = __shfl(x, 16 + lr, 64);
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int row = 32 * j + 16 * t2 + lr;
-        if (row < n) {
-#pragma unroll
-          for (int nn = 0; nn < NDV; ++nn) {
-            u32x2 t4;
-            t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
-            t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
-            *reinterpret_cast<u32x2*>(ob + (int64_t)(c0 + row) * ldx + dv0 + 16 * nn + 4 * lg) = t4;
-          }
-        }
-      }
-      if constexpr (QS == 2) pslot ^= 1;
-      store_pair(pslot);  // its previous readers finished before the last barrier
-      __syncthreads();
+      for (int e = 0; e < 8; ++e) lkey[e] = __shfl(x, 8 * lg + e, 64);
+      last = __shfl(x, 31, 64);
     }
 
-    // ---- state update: S += K_c^T V_c (gated: S = exp(L_last) S + K_c^T W V_c) ----
-    const int nts = (n + 31) >> 5;
+    // inter-block: O^T = S^T Q^T with the state before this block
+    f32x4 Ot[2][NDV];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int nn = 0; nn < NDV; ++nn) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = Sacc[2 * s][nn][i];
+          x[4 + i] = Sacc[2 * s + 1][nn][i];
+        }
+        u32x4 shi, slo;
+        split8(x, shi, slo);
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          Ot[t2][nn] = mfma16x16x32(shi, qf[t2][s], Ot[t2][nn]);
+          Ot[t2][nn] = mfma16x16x32(slo, qf[t2][s], Ot[t2][nn]);
+        }
+      }
+    }
     if constexpr (GATED) {
-      const float last = Lc[Cp - 1];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float f = fast_exp2(lrow[t2]);
+#pragma unroll
+        for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] *= f;
+      }
+    }
+
+    // intra-block scores P^T = K Q^T (two 16-key tiles), causal mask
+    f32x4 pt[2][2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pt[t2][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 kf =
+            *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 32 * s + 8 * lg, kswz<D>(krow)));
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) pt[t2][u] = mfma16x16x32(kf, qf[t2][s], pt[t2][u]);
+      }
+    }
+    u32x4 phi[2], plo[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int row = 16 * t2 + lr;
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 8 * lg + 4 * u + i;
+          float p = pt[t2][u][i];
+          if constexpr (GATED) p *= fast_exp2(lrow[t2] - lkey[4 * u + i]);
+          pv[4 * u + i] = (key <= row) ? p : 0.f;
+        }
+      split8(pv, phi[t2], plo[t2]);
+    }
+
+    // O^T += V^T P^T
+    u32x4 vf[NDV];
+#pragma unroll
+    for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_swz_raw<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+    lds_wait_all(vf);
+#pragma unroll
+    for (int nn = 0; nn < NDV; ++nn)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        Ot[t2][nn] = mfma16x16x32(vf[nn], phi[t2], Ot[t2][nn]);
+        Ot[t2][nn] = mfma16x16x32(vf[nn], plo[t2], Ot[t2][nn]);
+      }
+
+    // lane holds O^T[value col 16 nn + 4 lg + i][query row lr] of each tile
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int row = 16 * t2 + lr;
+      if (row < n) {
+#pragma unroll
+        for (int nn = 0; nn < NDV; ++nn) {
+          u32x2 t4;
+          t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
+          t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
+          *reinterpret_cast<u32x2*>(ob + (int64_t)(kLinBlock * b + row) * ldx + dv0 + 16 * nn + 4 * lg) = t4;
+        }
+      }
+    }
+
+    // state update: S += K_b^T V_b (gated: S = exp(L_last) S + K_b^T W V_b)
+    u32x4 kt[NDK];
+#pragma unroll
+    for (int t = 0; t < NDK; ++t)  // A operand: K^T rows pi(t, m) = columns of the K tile
+      kt[t] = tr_swz_raw<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
+    lds_wait_all(kt);
+    if constexpr (GATED) {
       const float decay = fast_exp2(last);
 #pragma unroll
       for (int t = 0; t < NDK; ++t)
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] *= decay;
-      for (int ts = 0; ts < nts; ++ts) {
-        const uint16_t* Kt = Ks + 32 * ts * D;
-        const uint16_t* Vt = Vs + 32 * ts * D;
-        // the lane's V operand holds tokens 32 ts + 8 (l / 16) + 0..7
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(Wc + 32 * ts + 8 * lg);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(Wc + 32 * ts + 8 * lg + 4);
-        const float wt[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        u32x4 vhi[NDV], vlo[NDV];
+      // the lane's V operand holds tokens 8 (l / 16) + 0..7 of the block
+      float wt[8];
 #pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) {
-          const u32x4 vf = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
-          float x[8];
+      for (int e = 0; e < 8; ++e) wt[e] = fast_exp2(last - lkey[e]);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            x[2 * p] = bf16_lo(vf[p]) * wt[2 * p];
-            x[2 * p + 1] = bf16_hi(vf[p]) * wt[2 * p + 1];
-          }
-          split8(x, vhi[nn], vlo[nn]);
+      for (int nn = 0; nn < NDV; ++nn) {
+        float x[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          x[2 * p] = bf16_lo(vf[nn][p]) * wt[2 * p];
+          x[2 * p + 1] = bf16_hi(vf[nn][p]) * wt[2 * p + 1];
         }
+        u32x4 vhi, vlo;
+        split8(x, vhi, vlo);
 #pragma unroll
         for (int t = 0; t < NDK; ++t) {
-          const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
-#pragma unroll
-          for (int nn = 0; nn < NDV; ++nn) {
-            Sacc[t][nn] = mfma16x16x32(kt, vhi[nn], Sacc[t][nn]);
-            Sacc[t][nn] = mfma16x16x32(kt, vlo[nn], Sacc[t][nn]);
-          }
+          Sacc[t][nn] = mfma16x16x32(kt[t], vhi, Sacc[t][nn]);
+          Sacc[t][nn] = mfma16x16x32(kt[t], vlo, Sacc[t][nn]);
         }
       }
     } else {
-      for (int ts = 0; ts < nts; ++ts) {
-        const uint16_t* Kt = Ks + 32 * ts * D;
-        const uint16_t* Vt = Vs + 32 * ts * D;
-        u32x4 vf[NDV];
 #pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) vf[nn] = tr_swz<D, false>(Vt, dv0 + 16 * nn + 4 * (lr & 3));
+      for (int t = 0; t < NDK; ++t)
 #pragma unroll
-        for (int t = 0; t < NDK; ++t) {
-          // A operand: K^T rows pi(t, m) = columns of the K tile
-          const u32x4 kt = tr_swz<D, true>(Kt, 32 * (t >> 1) + 8 * (lr & 3) + 4 * (t & 1));
-#pragma unroll
-          for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt, vf[nn], Sacc[t][nn]);
-        }
-      }
+        for (int nn = 0; nn < NDV; ++nn) Sacc[t][nn] = mfma16x16x32(kt[t], vf[nn], Sacc[t][nn]);
     }
   }
 
