@@ -37,7 +37,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # Extra flags per source. The paged kernels keep MFMA results in ordinary VGPRs:
 # their scores feed VALU softmax code, and the default placement in AGPRs
 # costs a copy per use.
-PER_FILE = {"k_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+PER_FILE = {"k_paged.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

@@ -48,6 +48,12 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
                                int B, int H_q, int H_kv, int D, float scale, void* workspace,
                                bool bf16, hipStream_t s);
 
+// VALU paged attention for fp32 I/O (decode with cu_q = NULL, or causal prefill).
+hipError_t launch_paged_simple_f32(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                   int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                   const int32_t* ctx, const int32_t* cu_q, int max_q_len, int B,
+                                   int H_q, int H_kv, int D, float scale, hipStream_t s);
+
 hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
                                 int64_t n_blocks, const int32_t* bt, int max_blocks,
                                 const int32_t* ctx,

@@ -1,0 +1,402 @@
+// Causal prefill attention over a paged KV cache of 16-token blocks for
+// gfx950, bf16 I/O (MFMA, FlashAttention-style). fp32 I/O takes the VALU
+// kernel in k_paged.hip.
+//
+// Method (page "推理框架适配Hybrid Model：KV Cache管理与算子调度实战", "P2"):
+//   §2.1  KV is cut into fixed 16-token blocks mapped through a per-request
+//         page (block) table.
+//   §2.3  prefill is a FlashAttention-class kernel: softmax attention of each
+//         new token over the request's cached tokens and the new ones before it.
+// Layout: pool [n_blocks][H_kv][16][D]; logical token p of request r lives in
+// block bt[r][p / 16] at offset p % 16; query head h reads KV head
+// h / (H_q / H_kv). Softmax is evaluated in base 2 on scores pre-multiplied by
+// scale * log2(e), with a running reference subtracted (fp32 throughout).
+#include <math.h>
+
+#include "hy_common.hpp"
+#include "hy_kernels.hpp"
+
+namespace hy {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSum = 65536.f;     // bound on a lane's p-sum before the reference moves
+constexpr float kMinusHuge = -0x1p100f;    // finite stand-in for -inf as a softmax reference
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+constexpr int kPrefillNR = 2;    // 16-row tiles per wave
+
+// ============================================================================
+// Causal prefill, bf16 (MFMA, FlashAttention-style). 1-D grid over (query
+// tile, H_kv, B), 4 waves. A workgroup takes QT = 64 NR / G query positions
+// of one request for all G query heads sharing KV head g (64 NR rows), so
+// every K/V tile staged in LDS serves G heads. Wave w owns 16 NR rows (NR
+// tiles of 16).
+//
+// K and V reach LDS through direct global-to-LDS loads (global_load_lds:
+// no registers hold the data in flight) in 32-key stages (two 16-token
+// blocks), kept in a ring of 4 stage buffers: stage st + 3 is requested
+// while stage st is used, so three stages of loads are in flight behind the
+// computation. Each lane's 16-byte load is aimed so that the tiles land
+// XOR-swizzled per row (the K score reads and the V transposing reads are
+// free of bank conflicts). Per stage:
+//   S^T = K Q^T   (two 16-key tiles; the key order inside each tile is
+//                  permuted so that a lane ends up with 8 consecutive keys of
+//                  its row, i.e. directly the B operand below)
+//   online softmax over the lane's row (see the stage body)
+//   O^T += V^T P^T (A = V^T fragment via transposing LDS reads, B = P^T
+//                  from registers)
+// Computing O^T rather than O keeps the softmax row, the score column and the
+// output column on the same lane, so rescaling needs no data movement.
+// ============================================================================
+template <int D>
+__host__ __device__ __forceinline__ int pf_kswz(int row) {  // chunk XOR of a K row of a stage
+  if constexpr (D == 128) return (row & 3) | ((row >> 1) & 12);
+  else return ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+template <int D>
+__host__ __device__ __forceinline__ int pf_vswz(int row) {  // chunk XOR of a V row of a stage (even)
+  if constexpr (D == 128) return ((row & 3) << 1) | (row & 8);
+  else return (row & 2) | (((row >> 3) & 1) << 2);
+}
+
+template <int D, int G, int NR>
+__global__ __launch_bounds__(256) void k_paged_prefill_bf16(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
+    int H_kv, float scale_log2, int n_qt, int n_req) {
+  constexpr int ROWS = 64 * NR; // rows (query position, head) per workgroup: 4 waves x 16 NR
+  constexpr int QT = ROWS / G;  // query positions per workgroup
+  constexpr int KS = D / 32;    // k steps over the head dim
+  constexpr int NDT = D / 16;   // 16-wide head-dim tiles of O^T
+  constexpr int KT = 32;        // keys per stage
+  constexpr int NB = 4;         // stage buffers in the ring
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // rows covered by one wave-wide 16-byte load
+  constexpr int IPB = 16 / RPI; // such loads per 16-token block
+  __shared__ __align__(16) uint16_t Ks[NB][KT * D];
+  __shared__ __align__(16) uint16_t Vs[NB][KT * D];
+
+  // 1-D grid, heaviest query tiles first (longest causal spans start early
+  // and short ones fill the tail); consecutive ids walk over (g, r), so the
+  // tiles of one (request, KV head) sit gridDim.x / n_qt ids apart, a
+  // multiple of 8 whenever H_kv * B is, and land on the same XCD and L2.
+  const int n_gr = H_kv * n_req;
+  const int qtile = n_qt - 1 - (int)blockIdx.x / n_gr;
+  const int g = (int)blockIdx.x % n_gr % H_kv, r = (int)blockIdx.x % n_gr / H_kv;
+  const int q0 = cu_q[r], ql = cu_q[r + 1] - q0;
+  const int i0 = qtile * QT;
+  if (i0 >= ql) return;
+  const int c = min(ctx[r], max_blocks * kBlock);
+  const int base_pos = c - ql;  // position of this request's first query
+  if (base_pos < 0 || n_blocks <= 0) return;  // more queries than context: invalid input
+  const int kend = min(c, base_pos + i0 + QT);
+  const int n_st = (kend + KT - 1) / KT;
+  const int pos_lo = base_pos + i0;  // smallest query position of the workgroup
+  const int32_t* btr = bt + (int64_t)r * max_blocks;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+
+  // ---- rows of this lane: tile rt covers wave rows 16 rt .. 16 rt + 15 ----
+  int row_pos[NR];   // query position inside the request (may be >= ql: padding)
+  int row_head[NR];
+  u32x4 qf[NR][KS];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    const int R = w * 16 * NR + 16 * rt + lr;
+    row_head[rt] = R / QT;
+    row_pos[rt] = i0 + R % QT;
+    const bool ok = row_pos[rt] < ql;
+    const uint16_t* qp = q + ((int64_t)(q0 + row_pos[rt]) * H_q + g * G + row_head[rt]) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[rt][s] = ok ? *reinterpret_cast<const u32x4*>(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x4 ot[NDT][NR];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // m_run: the row's softmax reference in the scaled (log2) domain, starting
+  // at a finite stand-in for -inf so that p = 2^(s - m) is +inf for any real
+  // score (forcing the first exact pass) and 0 for a masked one (never NaN).
+  // l_run: this lane's share of the row's sum of p.
+  float m_run[NR], l_run[NR];
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    m_run[rt] = kMinusHuge;
+    l_run[rt] = 0.f;
+  }
+
+  // ---- staging: wave w moves tensor (w & 1: K, V) of block (w >> 1) of
+  // each stage, IPB wave-wide 16-byte loads straight into LDS. The block id
+  // is wave-uniform (a scalar load, fetched one stage ahead of its use).
+  // Lane l of load i fills row 16 b + RPI i + l / CPR, chunk position
+  // l % CPR, so it fetches the logical chunk that the row's XOR maps there.
+  const int w_s = __builtin_amdgcn_readfirstlane(w);
+  const int sb = w_s >> 1;          // block of the stage this wave moves
+  const bool sv = (w_s & 1) != 0;   // V (else K)
+  const uint16_t* pool = sv ? v_pool : k_pool;
+  auto block_of = [&](int st) -> int32_t {  // raw table entry, validated at use
+    const int key = st * KT + kBlock * sb;
+    return (st < n_st && key < c) ? btr[key >> 4] : -1;
+  };
+  auto issue_stage = [&](int st, int32_t blk) {
+    if (blk < 0 || blk >= n_blocks) blk = 0;  // absent: any valid block, zeroed after landing
+    const uint16_t* src = pool + ((int64_t)blk * H_kv + g) * kBlock * D;
+    uint16_t* dst = (sv ? Vs[st % NB] : Ks[st % NB]) + kBlock * sb * D;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int tok = RPI * i + l / CPR;         // token within the block
+      const int row = kBlock * sb + tok;         // row within the stage
+      const int x = sv ? pf_vswz<D>(row) : pf_kswz<D>(row);
+      __builtin_amdgcn_global_load_lds(src + tok * D + 8 * ((l % CPR) ^ x),
+                                       (__attribute__((address_space(3))) void*)(dst + RPI * i * D),
+                                       16, 0, 0);
+    }
+  };
+  // rows of a landed stage that hold no valid key (past the context, or an
+  // absent block) are cleared by the wave that moved them: V must be finite
+  // there, as masked keys still meet it in P V with weight 0
+  auto clear_invalid = [&](int st, int32_t blk) {
+    const int key0 = st * KT + kBlock * sb;
+    const int nvalid = (blk < 0 || blk >= n_blocks) ? 0 : min(kBlock, max(0, c - key0));
+    if (nvalid == kBlock) return;
+    uint16_t* dst = (sv ? Vs[st % NB] : Ks[st % NB]) + kBlock * sb * D;
+    for (int e = l; e < kBlock * CPR; e += 64)
+      if (e / CPR >= nvalid) *reinterpret_cast<u32x4*>(dst + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+  };
+
+  // ---- scores S^T for the stage's 32 keys x this wave's rows ----
+  // Lane (lr, lg) receives keys 8 lg + 4 u + i of row tile rt.
+  auto scores = [&](const uint16_t* Kb, f32x4 (&sc)[2][NR]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) sc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 kf =
+            *reinterpret_cast<const u32x4*>(Kb + krow * D + 8 * ((4 * s + lg) ^ pf_kswz<D>(krow)));
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) sc[u][rt] = mfma16x16x32(kf, qf[rt][s], sc[u][rt]);
+      }
+    }
+  };
+
+  // ---- online softmax pieces ----
+  // p = 2^(s * scale_log2 - m_run), packed to bf16 pairs (the P^T operand);
+  // returns the lane's sum of the rounded p, the values P V actually uses.
+  auto probs = [&](const f32x4 (&sc)[2][NR], int rt, u32x4& pb) -> float {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[4 * u + i] = fast_exp2(__builtin_fmaf(sc[u][rt][i], scale_log2, -m_run[rt]));
+    float ps = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      pb[p2] = pack_bf16x2(x[2 * p2], x[2 * p2 + 1]);
+      ps = dot2_bf16(pb[p2], kOnesBf16x2, ps);
+    }
+    return ps;
+  };
+  auto mask = [&](int key0, f32x4 (&sc)[2][NR]) {  // keys beyond each row's position
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+      const int pos = base_pos + row_pos[rt];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 8 * lg + 4 * u + i > pos) sc[u][rt][i] = -INFINITY;
+    }
+  };
+  auto lane_max = [&](const f32x4 (&sc)[2][NR], int rt) -> float {
+    return fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
+                 fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
+  };
+
+  // ---- O^T += V^T P^T for the stage ----
+  // V^T rows 16 dt + lr (head dims), keys 8 lg + 0..7: two transposing reads
+  // per tile; source lane (lg, lr) addresses key row 8 lg + lr / 4 (+ 4),
+  // head dims 16 dt + 4 (lr % 4) + 0..3 (rows + 4 share the row's XOR). The
+  // reads are issued as plain instructions with one explicit wait: the
+  // compiler would otherwise drain every global-to-LDS load in flight before
+  // a transposing read, which would serialise the stage ring.
+  auto pv_acc = [&](const uint16_t* Vb, const u32x4 (&pb)[NR]) {
+    const int vrow = 8 * lg + (lr >> 2);
+    u32x4 vf[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int vcol = 16 * dt + 4 * (lr & 3);
+      const uint16_t* vp = Vb + vrow * D + 8 * ((vcol >> 3) ^ pf_vswz<D>(vrow)) + (vcol & 7);
+      const u32x2 v0 = ds_read_tr16_raw(vp);
+      const u32x2 v1 = ds_read_tr16_raw(vp + 4 * D);
+      vf[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    }
+    lds_wait_all(vf);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) ot[dt][rt] = mfma16x16x32(vf[dt], pb[rt], ot[dt][rt]);
+  };
+
+  // One 32-key stage. Softmax: the common case needs no cross-lane work. p is
+  // taken against the current reference m_run and each lane checks its own
+  // sum; only when some lane's sum exceeds kRescaleSum (a score above the
+  // reference by about log2(kRescaleSum), or the first keys of a row) does
+  // the wave take the exact path: per row, the maximum over the stage's keys
+  // across the four lanes holding it, a new reference, the rescale of the
+  // row's partial sums and accumulators, and p again.
+  auto compute = [&](auto diag, int st) {
+    const uint16_t* Kb = Ks[st % NB];
+    const uint16_t* Vb = Vs[st % NB];
+    f32x4 sc[2][NR];
+    u32x4 pb[NR];
+    float ps[NR];
+    scores(Kb, sc);
+    if constexpr (decltype(diag)::value) mask(st * KT, sc);
+    bool over = false;
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+      ps[rt] = probs(sc, rt, pb[rt]);
+      over |= !(ps[rt] <= kRescaleSum);  // also catches +inf
+    }
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float corr[NR];
+#pragma unroll
+      for (int rt = 0; rt < NR; ++rt) {
+        float mx = lane_max(sc, rt);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * scale_log2;  // -inf when every key of the stage is masked
+        corr[rt] = 1.f;
+        if (ms > m_run[rt]) {
+          corr[rt] = fast_exp2(m_run[rt] - ms);  // 0 on the row's first real key
+          l_run[rt] *= corr[rt];
+          m_run[rt] = ms;
+        }
+        ps[rt] = probs(sc, rt, pb[rt]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+          ot[dt][rt][0] *= corr[rt];
+          ot[dt][rt][1] *= corr[rt];
+          ot[dt][rt][2] *= corr[rt];
+          ot[dt][rt][3] *= corr[rt];
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) l_run[rt] += ps[rt];
+    pv_acc(Vb, pb);
+  };
+
+  // ---- the stage ring ----
+  // Each wave issues IPB loads per stage, and stages complete in order, so
+  // waiting for stage st leaves the IPB loads of each later stage already
+  // requested outstanding. Stage st + 3 goes into the buffer of stage st - 1,
+  // which every wave finished reading before the barrier of stage st.
+  int32_t blk_ring[NB];  // block ids of the stages in flight (wave-uniform)
+  // the Q fragments land first, so no later wait for them can drain the ring
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) {
+    blk_ring[i] = block_of(i);
+    if (i < n_st) issue_stage(i, blk_ring[i]);
+  }
+  blk_ring[NB - 1] = block_of(NB - 1);
+  auto stage = [&](auto diag, int st) {
+    const int ahead = n_st - 1 - st;  // stages requested after this one: min(ahead, NB - 2)
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPB));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPB));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int32_t blk = blk_ring[0];
+    if (st * KT + KT > c || blk < 0 || blk >= n_blocks) clear_invalid(st, blk);
+    // workgroup barrier without the release fence of __syncthreads, which
+    // would also drain the global-to-LDS loads still in flight: the stage's
+    // own loads were waited for above and LDS writes are waited for here
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (st + NB - 1 < n_st) issue_stage(st + NB - 1, blk_ring[NB - 1]);
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) blk_ring[i] = blk_ring[i + 1];
+    compute(diag, st);
+    // the block id after next is fetched after the compute: scalar loads
+    // share the LDS counter, so earlier it would delay the LDS reads above
+    blk_ring[NB - 1] = block_of(st + NB);
+  };
+  // stages whose keys all lie at or before the workgroup's first query
+  // position need no causal mask
+  const int n_plain = min(n_st, (pos_lo + 1) / KT);
+  int st = 0;
+  for (; st < n_plain; ++st) stage(BoolTag<false>{}, st);
+  for (; st < n_st; ++st) stage(BoolTag<true>{}, st);
+
+  // ---- normalise and store: lane holds O^T[d = 16 dt + 4 lg + i][row lr] ----
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
+    float L = l_run[rt];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const float inv = 1.f / L;
+    if (row_pos[rt] >= ql) continue;
+    uint16_t* op = o + ((int64_t)(q0 + row_pos[rt]) * H_q + g * G + row_head[rt]) * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x2 t;
+      t[0] = pack_bf16x2(ot[dt][rt][0] * inv, ot[dt][rt][1] * inv);
+      t[1] = pack_bf16x2(ot[dt][rt][2] * inv, ot[dt][rt][3] * inv);
+      *reinterpret_cast<u32x2*>(op + 16 * dt) = t;
+    }
+  }
+}
+
+hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                const int32_t* ctx,
+                                const int32_t* cu_q, int max_q_len, int B, int H_q, int H_kv,
+                                int D, float scale, bool bf16, hipStream_t s) {
+  if (B <= 0 || max_q_len <= 0) return hipSuccess;
+  const float sl2 = scale * kLog2e;
+  if (bf16) {
+    const int G = H_q / H_kv;
+#define HY_PP(DD, GG)                                                                          \
+  do {                                                                                         \
+    constexpr int QT_ = 64 * kPrefillNR / GG;                                                  \
+    const int n_qt = (max_q_len + QT_ - 1) / QT_;                                              \
+    dim3 grid((unsigned)(n_qt * H_kv * B));                                                    \
+    hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR>), grid, dim3(256), 0, s, (const uint16_t*)q, \
+                       (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
+                       bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                    \
+  } while (0)
+#define HY_PP_G(DD)                   \
+  switch (G) {                        \
+    case 1: HY_PP(DD, 1); break;      \
+    case 2: HY_PP(DD, 2); break;      \
+    case 4: HY_PP(DD, 4); break;      \
+    case 8: HY_PP(DD, 8); break;      \
+    default: return hipErrorInvalidValue; \
+  }
+    if (D == 128) {
+      HY_PP_G(128)
+    } else {
+      HY_PP_G(64)
+    }
+#undef HY_PP_G
+#undef HY_PP
+    return hipGetLastError();
+  }
+  return launch_paged_simple_f32(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, cu_q,
+                                 max_q_len, B, H_q, H_kv, D, scale, s);
+}
+
+}  // namespace hy
