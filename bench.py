@@ -214,8 +214,17 @@ def component_times(wl, reps=3):
 
 PMC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                            "paged_decode_hbm_traffic.md")
-DECODE_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_attn_amd",
-                             "csrc", "k_paged.hip")
+# sources that make up the paged-decode kernel (hashed together, in this order)
+DECODE_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_attention_attn_amd",
+                               "csrc", f) for f in ("k_paged.hip", "hy_common.hpp", "hy_kernels.hpp")]
+
+
+def decode_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -224,14 +233,14 @@ def measured_traffic():
     The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch of
     k_paged_decode_bf16 on this workload), the factors that map each counter
     onto bytes (from a plain copy of known size) and the SHA-256 of the
-    kernel source the counters were taken with. Returns None when the file is
-    missing or the source has changed since.
+    kernel's sources the counters were taken with (k_paged.hip and the two
+    headers it includes). Returns None when the file is missing or a source
+    has changed since.
     """
-    import hashlib
     import re
     try:
         text = open(PMC_SUMMARY).read()
-        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+        src = decode_source_sha256()
     except OSError:
         return None
     fields = dict(re.findall(r"^- (\w+): (\S+)$", text, re.M))
