@@ -146,9 +146,10 @@ class Workload:
         return self.n_d * self.H * (2 * self.D * self.D * 4 + 4 * self.D * 2 + (4 if gated else 0))
 
     def linear_prefill_flops(self, gated=False):
-        C, D, T = W["chunk"], self.D, W["prefill_len"]
-        # per token-head: Q.S (2D^2) + S update (2D^2) + causal intra-chunk (C+1)D (QK^T and PV);
-        # the gates' scalings are elementwise and not counted
+        # the bf16 kernel works in 32-token blocks whatever the chunk size (the sums are the
+        # same), so its work per token-head is Q.S (2D^2) + S update (2D^2) + the causal
+        # intra-block part 2 (32 + 1) D; the gates' scalings are elementwise and not counted
+        C, D, T = 32, self.D, W["prefill_len"]
         per_tok = 4 * D * D + 2 * (C + 1) * D
         return self.n_p * T * self.H * per_tok
 
