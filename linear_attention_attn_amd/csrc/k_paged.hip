@@ -138,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 }
 
 // ============================================================================
-// Decode, bf16. 1-D grid over (worker, KV head g), head fastest, 4 waves;
+// Decode, bf16. 1-D grid over (KV head g, worker), worker fastest, 4 waves;
 // each workgroup walks the (request, partition) items worker, worker +
 // n_workers, ... for its KV head.
 // Wave w of a workgroup takes blocks w, w + 4, ... of the partition.
@@ -187,10 +187,13 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ __align__(16) float s_acc[NW][G][D];
 
-  // 1-D grid, KV head fastest: the H_kv workgroups of an item run side by
-  // side and read each block's heads, which are adjacent in the pool
-  const int g = (int)blockIdx.x % H_kv;
-  const int worker = (int)blockIdx.x / H_kv, n_workers = (int)gridDim.x / H_kv;
+  // 1-D grid, worker fastest: consecutive workgroups go to consecutive XCDs,
+  // so with a worker count that is a multiple of 8 every head of an item
+  // runs on the same XCD, whose address translations then cover only the
+  // pool pages of its own items
+  const int n_workers = (int)gridDim.x / H_kv;
+  const int g = (int)blockIdx.x / n_workers;
+  const int worker = (int)blockIdx.x - g * n_workers;
   const int total = cu_parts[B];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
   const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index, as a scalar
@@ -546,7 +549,8 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   if (e != hipSuccess) return e;
   // enough workers to fill the chip a few times over; each walks items with stride gridDim.x
   const long bound = (long)B * plan.max_parts;
-  const unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
+  unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
+  if (workers > 8) workers &= ~7u;  // a multiple of the 8 XCDs (see the kernel)
   dim3 grid(workers * (unsigned)H_kv), block(256);
 #define HY_PD(DD, GG)                                                                         \
   do {                                                                                        \
