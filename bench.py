@@ -386,7 +386,7 @@ def main():
                     help="only run a plain 2 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the hybrid attention step has no multi-GPU path here", file=sys.stderr)
         sys.exit(2)
     import torch
