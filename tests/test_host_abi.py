@@ -141,6 +141,47 @@ def test_argument_validation_before_launch():
     hy.hyattn_state_pool_destroy(h)
 
 
+def test_gated_argument_validation_before_launch():
+    """Gated state update (the Mamba/RWKV-style layers of P2 §1.3, read as one
+    scalar forget factor per token and head): the factors are a required
+    input of the gated calls and belong to linear layers only; both mistakes
+    are refused on the host before any launch."""
+    h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 2, 4, 2, 128)
+    P = FAKE
+    cases = [
+        (lambda: hy.hyattn_linear_decode_gated(h, 0, P, P, P, None, P, P, 1, hy.BF16, 0),
+         hy.ERR_INVALID_ARG),                                               # no log_gamma
+        (lambda: hy.hyattn_linear_prefill_chunked_gated(h, 0, P, P, P, None, P, P, P, 1, 64,
+                                                        hy.BF16, 0), hy.ERR_INVALID_ARG),
+        (lambda: hy.hyattn_linear_decode_gated(h, 2, P, P, P, P, P, P, 1, hy.BF16, 0),
+         hy.ERR_INVALID_ARG),                                               # layer out of range
+        (lambda: hy.hyattn_linear_prefill_chunked_gated(h, 0, P, P, P, P, P, P, P, 1, 17,
+                                                        hy.BF16, 0), hy.ERR_UNSUPPORTED),
+        (lambda: hy.hyattn_linear_decode_gated(h, 0, P, P, P, P, P, P, -1, hy.BF16, 0),
+         hy.ERR_INVALID_ARG),
+    ]
+    for i, (fn, st) in enumerate(cases):
+        with pytest.raises(hy.HyattnError) as e:
+            fn()
+        assert e.value.status == st, (i, e.value)
+    # zero-sized gated calls succeed without touching the device, log_gamma or not
+    hy.hyattn_linear_decode_gated(h, 0, None, None, None, None, None, None, 0, hy.BF16, 0)
+    hy.hyattn_linear_prefill_chunked_gated(h, 0, None, None, None, None, None, None, None, 0, 64,
+                                           hy.BF16, 0)
+    # a full layer that carries forget factors is a caller mistake
+    b = hy.make_batch(n_prefill=0, n_decode=1, decode_slots=FAKE, H=2, H_kv=2, D=128,
+                      chunk_size=64, dtype=hy.BF16, block_tables=FAKE, context_lens=FAKE,
+                      cu_q_lens=FAKE, max_blocks_per_seq=4, n_blocks=8, max_context=64,
+                      workspace=FAKE, workspace_bytes=1 << 20, scale=1.0)
+    lin = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, log_gamma=FAKE)
+    full = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, k_pool=FAKE, v_pool=FAKE, log_gamma=FAKE)
+    with pytest.raises(hy.HyattnError) as e:
+        hy.hyattn_hybrid_step([hy.LAYER_LINEAR, hy.LAYER_FULL], 2, [lin, full], b, h, 0)
+    assert e.value.status == hy.ERR_INVALID_ARG
+    assert "log_gamma" in e.value.message
+    hy.hyattn_state_pool_destroy(h)
+
+
 def test_unknown_layer_type_rejected_before_any_launch():
     """P1 §4.3: an unsupported attention type is refused; nothing is launched."""
     h = hy.hyattn_state_pool_create(FAKE, 1 << 40, 2, 4, 2, 128)
