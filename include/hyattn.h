@@ -83,7 +83,8 @@ size_t hyattn_state_pool_bytes(int n_linear_layers, int n_slots, int H, int D);
 
 /* Wrap a caller-owned device buffer of at least hyattn_state_pool_bytes()
  * bytes (16-byte aligned). The handle owns only host bookkeeping; all slots
- * start free. */
+ * start free. D is 64 or 128 and H * D below 2^23 (HYATTN_ERR_UNSUPPORTED
+ * otherwise). */
 hyattn_status hyattn_state_pool_create(void* dev_buf, size_t bytes, int n_linear_layers,
                                        int n_slots, int H, int D, hyattn_state_pool** out);
 

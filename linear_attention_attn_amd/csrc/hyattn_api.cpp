@@ -188,6 +188,9 @@ hyattn_status hyattn_state_pool_create(void* dev_buf, size_t bytes, int n_linear
     return fail(HYATTN_ERR_INVALID_ARG, "pool dims must be positive (L=%d, slots=%d, H=%d)",
                 n_linear_layers, n_slots, H);
   if (!d_ok(D)) return fail(HYATTN_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+  if ((int64_t)H * D >= (1 << 23))
+    return fail(HYATTN_ERR_UNSUPPORTED, "H * D = %lld not supported (at most 2^23 - 1)",
+                (long long)H * D);
   const size_t need = hyattn_state_pool_bytes(n_linear_layers, n_slots, H, D);
   if (need == 0) return fail(HYATTN_ERR_INVALID_ARG, "pool size overflows");
   if (!dev_buf) return fail(HYATTN_ERR_INVALID_ARG, "device buffer is NULL");

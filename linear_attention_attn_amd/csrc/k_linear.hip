@@ -55,14 +55,21 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
                                                        const T* __restrict__ k,
                                                        const T* __restrict__ v, T* __restrict__ o,
                                                        const float* __restrict__ log_gamma,
-                                                       const int32_t* __restrict__ slots, int H) {
+                                                       const int32_t* __restrict__ slots, int H,
+                                                       int n_units) {
   constexpr int C4 = D / 4;      // threads across a row (4 floats each)
   constexpr int RG = 256 / C4;   // row groups
   constexpr int RP = D / RG;     // rows per thread
   __shared__ float sq[D], sk[D], sv[D];
   __shared__ float red[RG][D];
 
-  const int unit = blockIdx.x;  // r * H + h
+  // XCD-major order: workgroup ids go round-robin over the 8 XCDs, and XCD x
+  // (ids x, x + 8, ...) takes the consecutive units x P .. x P + P - 1, so
+  // each XCD streams one contiguous eighth of the listed states. The grid has
+  // 8 P ids (P = ceil(n_units / 8)); ids past the last unit exit.
+  const int per = (int)gridDim.x >> 3;
+  const int unit = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);  // r * H + h
+  if (unit >= n_units) return;
   const int r = unit / H;
   const int h = unit - r * H;
   const int slot = slots[r];
@@ -121,10 +128,10 @@ hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q,
                                 const int32_t* slots, int B, int H, int D, bool bf16,
                                 hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  dim3 grid((unsigned)(B * H)), block(256);
+  dim3 grid((unsigned)(8 * ((B * H + 7) / 8))), block(256);
 #define HY_DEC(DD, TT, GG)                                                                    \
   hipLaunchKernelGGL((k_linear_decode<DD, TT, GG>), grid, block, 0, s, layer_states, n_slots, \
-                     (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, log_gamma, slots, H)
+                     (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, log_gamma, slots, H, B * H)
 #define HY_DEC_G(DD, TT)       \
   if (log_gamma)               \
     HY_DEC(DD, TT, true);      \
@@ -414,22 +421,32 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   const uint16_t* vb = v + (int64_t)tok0 * ldx + (int64_t)h * D;
   uint16_t* ob = o + (int64_t)tok0 * ldx + (int64_t)h * D;
 
-  // ---- block loads: wave w moves pieces w IPB .. w IPB + IPB - 1 of the
-  // block's 3 IPT pieces (K pieces, then V, then Q; RPI rows each). Rows past
+  // ---- block loads: the block's 3 IPT pieces (K pieces, then V, then Q; RPI
+  // rows each) go round-robin over the waves, so load i of wave w is piece
+  // 4 i + w: its tensor, 4 i / IPT, is known at compile time and its rows are
+  // piece (4 i) % IPT + w of that tensor. A lane's source address is the
+  // block's first token row (a wave-uniform 64-bit base) plus a small row
+  // offset (24-bit multiply; the launcher checks that H D fits). Rows past
   // the request's end load its last token (finite data; V rows are cleared
   // before use, K and Q rows only meet masked scores or unstored outputs).
+  static_assert(IPT % 4 == 0, "pieces of a tensor split evenly over 4 waves");
+  auto piece_row = [&](int i) { return ((4 * i) % IPT + w) * RPI + l / CPR; };
+  auto piece_swz = [&](int i, int row) {
+    const int tensor = 4 * i / IPT;
+    return tensor == 0 ? kswz<D>(row) : (tensor == 1 ? vswz<D>(row) : qswz<D>(row));
+  };
   auto issue = [&](int b, int sl) {
     uint16_t* base = lds_h + sl * R::SLOT;
+    const int64_t blk = (int64_t)(kLinBlock * b) * ldx;
+    const int last = T - 1 - kLinBlock * b;  // last valid row of the block
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      const int ig = w * IPB + i;
-      const int tensor = ig / IPT, piece = ig - (ig / IPT) * IPT;
-      const int row = piece * RPI + l / CPR;
-      const int tok = min(kLinBlock * b + row, T - 1);
-      const int x = tensor == 0 ? kswz<D>(row) : (tensor == 1 ? vswz<D>(row) : qswz<D>(row));
-      const uint16_t* src = (tensor == 0 ? kb : (tensor == 1 ? vb : qb)) + (int64_t)tok * ldx +
-                            8 * ((l % CPR) ^ x);
-      uint16_t* dst = base + tensor * TILE + piece * RPI * D;
+      const int tensor = 4 * i / IPT;
+      const int row = piece_row(i);
+      const int rr = min(row, last);
+      const uint32_t off = (uint32_t)__mul24(rr, (int)ldx) + 8 * ((l % CPR) ^ piece_swz(i, row));
+      const uint16_t* src = (tensor == 0 ? kb : (tensor == 1 ? vb : qb)) + blk + off;
+      uint16_t* dst = base + tensor * TILE + ((4 * i) % IPT + w) * RPI * D;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
     if constexpr (GATED) {  // this wave's copy of the block's forget factors (lanes 32..63 repeat)
@@ -444,11 +461,10 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     uint16_t* base = lds_h + sl * R::SLOT;
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      const int ig = w * IPB + i;
-      const int tensor = ig / IPT, piece = ig - (ig / IPT) * IPT;
-      const int row = piece * RPI + l / CPR;
-      if (tensor == 1 && row >= n)
-        *reinterpret_cast<u32x4*>(base + TILE + piece * RPI * D + 8 * l) = u32x4{0u, 0u, 0u, 0u};
+      const int row = piece_row(i);
+      if (4 * i / IPT == 1 && row >= n)
+        *reinterpret_cast<u32x4*>(base + TILE + ((4 * i) % IPT + w) * RPI * D + 8 * l) =
+            u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -591,12 +607,13 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     for (int t2 = 0; t2 < 2; ++t2) {
       const int row = 16 * t2 + lr;
       if (row < n) {
+        uint16_t* orow = ob + (int64_t)(kLinBlock * b) * ldx + (uint32_t)(row * (int)ldx + dv0 + 4 * lg);
 #pragma unroll
         for (int nn = 0; nn < NDV; ++nn) {
           u32x2 t4;
           t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
           t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
-          *reinterpret_cast<u32x2*>(ob + (int64_t)(kLinBlock * b + row) * ldx + dv0 + 16 * nn + 4 * lg) = t4;
+          *reinterpret_cast<u32x2*>(orow + 16 * nn) = t4;
         }
       }
     }
@@ -670,6 +687,8 @@ hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q
   const bool gated = log_gamma != nullptr;
   hipError_t e;
   if (bf16) {
+    // the block loads form a lane's row offset with a 24-bit multiply by H D
+    if ((int64_t)H * D >= (1 << 23)) return hipErrorInvalidValue;
 #define HY_LP(DD, GG)                                                                          \
   do {                                                                                         \
     const size_t lds = prefill_bf16_lds_bytes<DD>(chunk, GG);                                  \

@@ -60,6 +60,49 @@ __host__ __device__ __forceinline__ int pf_vswz(int row) {  // chunk XOR of a V 
   else return (row & 2) | (((row >> 3) & 1) << 2);
 }
 
+// All transposing reads of a stage's V operand as one opaque block: D / 16
+// fragments, each two reads 4 rows apart, fragment i from LDS byte address
+// a[i]. Opaque, so the compiler does not drain the global-to-LDS loads in
+// flight before it (it would before its own transposing reads); it also does
+// not see the block's register writes, so the leading s_nop provides the wait
+// states that an MFMA issued just before the block needs when it still reads
+// a register the block overwrites (the compiler inserts them for its own LDS
+// loads). The caller waits (lds_wait_all) before using the fragments.
+template <int D> __device__ __forceinline__ void tr_block(const uint32_t (&a)[D / 16], u32x4 (&vf)[D / 16]);
+template <> __device__ __forceinline__ void tr_block<128>(const uint32_t (&a)[8], u32x4 (&vf)[8]) {
+  u32x2 r[16];
+  asm volatile(
+      "s_nop 7\n"
+      "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %16 offset:1024\n"
+      "ds_read_b64_tr_b16 %2, %17\n ds_read_b64_tr_b16 %3, %17 offset:1024\n"
+      "ds_read_b64_tr_b16 %4, %18\n ds_read_b64_tr_b16 %5, %18 offset:1024\n"
+      "ds_read_b64_tr_b16 %6, %19\n ds_read_b64_tr_b16 %7, %19 offset:1024\n"
+      "ds_read_b64_tr_b16 %8, %20\n ds_read_b64_tr_b16 %9, %20 offset:1024\n"
+      "ds_read_b64_tr_b16 %10, %21\n ds_read_b64_tr_b16 %11, %21 offset:1024\n"
+      "ds_read_b64_tr_b16 %12, %22\n ds_read_b64_tr_b16 %13, %22 offset:1024\n"
+      "ds_read_b64_tr_b16 %14, %23\n ds_read_b64_tr_b16 %15, %23 offset:1024"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vf[i] = u32x4{r[2 * i][0], r[2 * i][1], r[2 * i + 1][0], r[2 * i + 1][1]};
+}
+template <> __device__ __forceinline__ void tr_block<64>(const uint32_t (&a)[4], u32x4 (&vf)[4]) {
+  u32x2 r[8];
+  asm volatile(
+      "s_nop 7\n"
+      "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %8 offset:512\n"
+      "ds_read_b64_tr_b16 %2, %9\n ds_read_b64_tr_b16 %3, %9 offset:512\n"
+      "ds_read_b64_tr_b16 %4, %10\n ds_read_b64_tr_b16 %5, %10 offset:512\n"
+      "ds_read_b64_tr_b16 %6, %11\n ds_read_b64_tr_b16 %7, %11 offset:512"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vf[i] = u32x4{r[2 * i][0], r[2 * i][1], r[2 * i + 1][0], r[2 * i + 1][1]};
+}
+
 template <int D, int G, int NR>
 __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
@@ -78,13 +121,20 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   __shared__ __align__(16) uint16_t Ks[NB][KT * D];
   __shared__ __align__(16) uint16_t Vs[NB][KT * D];
 
-  // 1-D grid, heaviest query tiles first (longest causal spans start early
-  // and short ones fill the tail); consecutive ids walk over (g, r), so the
-  // tiles of one (request, KV head) sit gridDim.x / n_qt ids apart, a
-  // multiple of 8 whenever H_kv * B is, and land on the same XCD and L2.
+  // 1-D grid in XCD-major order. Workgroup ids go round-robin over the 8
+  // XCDs, so XCD x runs ids x, x + 8, ...; its j-th one takes (request, KV
+  // head) pair 8 (j / n_qt) + x and query tile n_qt - 1 - j % n_qt. Each XCD
+  // thus works through its pairs one after another, all query tiles of a
+  // pair together, heaviest (longest causal span) first: the tiles in flight
+  // on an XCD stream the same pair's keys, which its L2 then holds, and the
+  // shortest tiles fill the tail. Ids past the last pair exit at once.
   const int n_gr = H_kv * n_req;
-  const int qtile = n_qt - 1 - (int)blockIdx.x / n_gr;
-  const int g = (int)blockIdx.x % n_gr % H_kv, r = (int)blockIdx.x % n_gr / H_kv;
+  const int xcd = (int)blockIdx.x & 7, jx = (int)blockIdx.x >> 3;
+  const int pslot = jx / n_qt;
+  const int pair = pslot * 8 + xcd;
+  if (pair >= n_gr) return;
+  const int qtile = n_qt - 1 - (jx - pslot * n_qt);
+  const int g = pair % H_kv, r = pair / H_kv;
   const int q0 = cu_q[r], ql = cu_q[r + 1] - q0;
   const int i0 = qtile * QT;
   if (i0 >= ql) return;
@@ -225,20 +275,21 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   // V^T rows 16 dt + lr (head dims), keys 8 lg + 0..7: two transposing reads
   // per tile; source lane (lg, lr) addresses key row 8 lg + lr / 4 (+ 4),
   // head dims 16 dt + 4 (lr % 4) + 0..3 (rows + 4 share the row's XOR). The
-  // reads are issued as plain instructions with one explicit wait: the
-  // compiler would otherwise drain every global-to-LDS load in flight before
-  // a transposing read, which would serialise the stage ring.
-  auto pv_acc = [&](const uint16_t* Vb, const u32x4 (&pb)[NR]) {
+  // reads are requested right after the scores (tr_block), so they complete
+  // while the softmax runs; one explicit wait precedes the products.
+  auto pv_load = [&](const uint16_t* Vb, u32x4 (&vf)[NDT]) {
     const int vrow = 8 * lg + (lr >> 2);
-    u32x4 vf[NDT];
+    uint32_t a[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const int vcol = 16 * dt + 4 * (lr & 3);
       const uint16_t* vp = Vb + vrow * D + 8 * ((vcol >> 3) ^ pf_vswz<D>(vrow)) + (vcol & 7);
-      const u32x2 v0 = ds_read_tr16_raw(vp);
-      const u32x2 v1 = ds_read_tr16_raw(vp + 4 * D);
-      vf[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      a[dt] = static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)vp));
     }
+    tr_block<D>(a, vf);
+  };
+  auto pv_acc = [&](u32x4 (&vf)[NDT], const u32x4 (&pb)[NR]) {
     lds_wait_all(vf);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -260,6 +311,8 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     u32x4 pb[NR];
     float ps[NR];
     scores(Kb, sc);
+    u32x4 vf[NDT];
+    pv_load(Vb, vf);
     if constexpr (decltype(diag)::value) mask(st * KT, sc);
     bool over = false;
 #pragma unroll
@@ -295,7 +348,7 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     }
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) l_run[rt] += ps[rt];
-    pv_acc(Vb, pb);
+    pv_acc(vf, pb);
   };
 
   // ---- the stage ring ----
@@ -373,7 +426,7 @@ hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, cons
   do {                                                                                         \
     constexpr int QT_ = 64 * kPrefillNR / GG;                                                  \
     const int n_qt = (max_q_len + QT_ - 1) / QT_;                                              \
-    dim3 grid((unsigned)(n_qt * H_kv * B));                                                    \
+    dim3 grid((unsigned)(n_qt * 8 * ((H_kv * B + 7) / 8)));                                    \
     hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR>), grid, dim3(256), 0, s, (const uint16_t*)q, \
                        (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
                        bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                    \

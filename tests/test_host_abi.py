@@ -99,7 +99,8 @@ def test_pool_create_validation():
                      ((FAKE, 100, 1, 1, 1, 64), hy.ERR_INVALID_ARG),
                      ((FAKE + 4, 1 << 30, 1, 1, 1, 64), hy.ERR_INVALID_ARG),
                      ((FAKE, 1 << 30, 1, 1, 1, 96), hy.ERR_UNSUPPORTED),
-                     ((FAKE, 1 << 30, 0, 1, 1, 64), hy.ERR_INVALID_ARG)):
+                     ((FAKE, 1 << 30, 0, 1, 1, 64), hy.ERR_INVALID_ARG),
+                     ((FAKE, 1 << 40, 1, 1, 65536, 128), hy.ERR_UNSUPPORTED)):  # H D = 2^23
         with pytest.raises(hy.HyattnError) as e:
             hy.hyattn_state_pool_create(*args)
         assert e.value.status == st, args
