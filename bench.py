@@ -162,8 +162,10 @@ class Workload:
 
 
 # ------------------------------------------------------------- components --
-def component_times(wl, reps=3):
-    """Per-call device time of each layer operation, HIP events on torch's stream."""
+def component_times(wl, reps=3, inner=5):
+    """Per-call device time of each layer operation, HIP events on torch's stream: the
+    median over `reps` event pairs, each around `inner` back-to-back calls (so the host's
+    launch latency of the first call does not count against a sub-millisecond kernel)."""
     import torch
     hy = wl.hy
     st = torch.cuda.current_stream()
@@ -205,10 +207,11 @@ def component_times(wl, reps=3):
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(st)
-            fn()
+            for _ in range(inner):
+                fn()
             e1.record(st)
             e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
+            ts.append(e0.elapsed_time(e1) / inner)
         out[name] = float(np.median(ts))
     return out
 

@@ -495,15 +495,6 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
     const uint16_t* Vt = Kt + TILE;
     const uint16_t* Qt = Vt + TILE;
 
-    u32x4 qf[2][KS];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int row = 16 * t2 + lr;
-        qf[t2][s] = *reinterpret_cast<const u32x4*>(Qt + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
-      }
-
     // gated: L of the lane's query rows and keys, and of the block's last token
     float lrow[2] = {0.f, 0.f}, lkey[8], last = 0.f;
     if constexpr (GATED) {
@@ -521,14 +512,37 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
       last = __shfl(x, 31, 64);
     }
 
-    // inter-block: O^T = S^T Q^T with the state before this block
+    // inter-block O^T = S^T Q^T (state before this block) and intra-block
+    // scores P^T = K Q^T (two 16-key tiles), one 32-wide k step at a time so
+    // each Q fragment serves both products; the fragments of step s + 1 are
+    // requested before the products of step s
     f32x4 Ot[2][NDV];
+    f32x4 pt[2][2];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
       for (int nn = 0; nn < NDV; ++nn) Ot[t2][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+      for (int u = 0; u < 2; ++u) pt[t2][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto load_qk = [&](int s, u32x4 (&qf)[2], u32x4 (&kf)[2]) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int row = 16 * t2 + lr;
+        qf[t2] = *reinterpret_cast<const u32x4*>(Qt + swz_off<D>(row, 32 * s + 8 * lg, qswz<D>(row)));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
+        kf[u] = *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 32 * s + 8 * lg, kswz<D>(krow)));
+      }
+    };
+    u32x4 qf[2], kf[2];
+    load_qk(0, qf, kf);
+#pragma unroll
     for (int s = 0; s < KS; ++s) {
+      u32x4 qn[2], kn[2];
+      if (s + 1 < KS) load_qk(s + 1, qn, kn);
 #pragma unroll
       for (int nn = 0; nn < NDV; ++nn) {
         float x[8];
@@ -541,8 +555,19 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
         split8(x, shi, slo);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
-          Ot[t2][nn] = mfma16x16x32(shi, qf[t2][s], Ot[t2][nn]);
-          Ot[t2][nn] = mfma16x16x32(slo, qf[t2][s], Ot[t2][nn]);
+          Ot[t2][nn] = mfma16x16x32(shi, qf[t2], Ot[t2][nn]);
+          Ot[t2][nn] = mfma16x16x32(slo, qf[t2], Ot[t2][nn]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) pt[t2][u] = mfma16x16x32(kf[u], qf[t2], pt[t2][u]);
+      if (s + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          qf[i] = qn[i];
+          kf[i] = kn[i];
         }
       }
     }
@@ -555,23 +580,6 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
       }
     }
 
-    // intra-block scores P^T = K Q^T (two 16-key tiles), causal mask
-    f32x4 pt[2][2];
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) pt[t2][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int krow = 8 * (lr >> 2) + 4 * u + (lr & 3);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 kf =
-            *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 32 * s + 8 * lg, kswz<D>(krow)));
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) pt[t2][u] = mfma16x16x32(kf, qf[t2][s], pt[t2][u]);
-      }
-    }
     u32x4 phi[2], plo[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
