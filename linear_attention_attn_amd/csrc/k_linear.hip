@@ -403,6 +403,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   using R = LinRing<D, GATED>;
   constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = R::CPR, RPI = R::RPI;
   constexpr int TILE = R::TILE, IPT = R::IPT, IPB = R::IPB, VMB = R::VMB;
+  constexpr int OSTORES = NDV == 2 ? 2 : 2 * NDV;  // output store instructions per wave per block
   extern __shared__ __align__(16) uint16_t lds_h[];
 
   const int unit = blockIdx.x;
@@ -484,9 +485,16 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   for (int b = 0; b < nb; ++b) {
     const int sl = b % kLinRing;
     const int n = min(kLinBlock, T - kLinBlock * b);
-    // this wave's loads of block b have landed (block b + 1's may still fly)
-    if (b + 1 < nb) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // this wave's loads of block b have landed (block b + 1's may still fly).
+    // Vector-memory operations retire in issue order, and the output stores of
+    // block b - 1 were issued after block b + 1's loads: when all of them were
+    // issued (block b - 1 was whole), they are left outstanding too.
+    if (b + 1 < nb) {
+      if (b > 0 && kLinBlock * b <= T) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB + OSTORES));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
     if (n < kLinBlock) clear_tail(sl, n);
     lds_barrier();  // block b visible to all waves; block b - 1's slot is free
     if (b + kLinRing - 1 < nb) issue(b + kLinRing - 1, (b + kLinRing - 1) % kLinRing);
@@ -611,17 +619,41 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
       }
 
     // lane holds O^T[value col 16 nn + 4 lg + i][query row lr] of each tile
+    if constexpr (NDV == 2) {
+      // lanes lg and lg ^ 1 (16 apart) swap a half so that each holds 8
+      // consecutive columns of its row: lg even columns 4 lg .. 4 lg + 7,
+      // lg odd columns 16 + 4 (lg - 1) .. + 7; every row of the wave's slice
+      // then leaves as four aligned 16-byte pieces, whole 64-byte segments
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int row = 16 * t2 + lr;
-      if (row < n) {
-        uint16_t* orow = ob + (int64_t)(kLinBlock * b) * ldx + (uint32_t)(row * (int)ldx + dv0 + 4 * lg);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int row = 16 * t2 + lr;
+        uint32_t a0 = pack_bf16x2(Ot[t2][0][0], Ot[t2][0][1]);
+        uint32_t a1 = pack_bf16x2(Ot[t2][0][2], Ot[t2][0][3]);
+        uint32_t b0 = pack_bf16x2(Ot[t2][1][0], Ot[t2][1][1]);
+        uint32_t b1 = pack_bf16x2(Ot[t2][1][2], Ot[t2][1][3]);
+        const bool even = (lg & 1) == 0;
+        const uint32_t s0 = even ? b0 : a0, s1 = even ? b1 : a1;  // the half the partner keeps
+        const uint32_t r0 = __shfl_xor(s0, 16), r1 = __shfl_xor(s1, 16);
+        const u32x4 piece = even ? u32x4{a0, a1, r0, r1} : u32x4{r0, r1, b0, b1};
+        const int col = even ? 4 * lg : 16 + 4 * (lg - 1);
+        if (row < n) {
+          uint16_t* orow = ob + (int64_t)(kLinBlock * b) * ldx + (uint32_t)(row * (int)ldx + dv0 + col);
+          *reinterpret_cast<u32x4*>(orow) = piece;
+        }
+      }
+    } else {
 #pragma unroll
-        for (int nn = 0; nn < NDV; ++nn) {
-          u32x2 t4;
-          t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
-          t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
-          *reinterpret_cast<u32x2*>(orow + 16 * nn) = t4;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int row = 16 * t2 + lr;
+        if (row < n) {
+          uint16_t* orow = ob + (int64_t)(kLinBlock * b) * ldx + (uint32_t)(row * (int)ldx + dv0 + 4 * lg);
+#pragma unroll
+          for (int nn = 0; nn < NDV; ++nn) {
+            u32x2 t4;
+            t4[0] = pack_bf16x2(Ot[t2][nn][0], Ot[t2][nn][1]);
+            t4[1] = pack_bf16x2(Ot[t2][nn][2], Ot[t2][nn][3]);
+            *reinterpret_cast<u32x2*>(orow + 16 * nn) = t4;
+          }
         }
       }
     }
