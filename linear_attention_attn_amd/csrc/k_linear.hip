@@ -403,7 +403,6 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   using R = LinRing<D, GATED>;
   constexpr int NDV = Cfg::NDV, NDK = Cfg::NDK, KS = Cfg::KS, CPR = R::CPR, RPI = R::RPI;
   constexpr int TILE = R::TILE, IPT = R::IPT, IPB = R::IPB, VMB = R::VMB;
-  constexpr int OSTORES = NDV == 2 ? 2 : 2 * NDV;  // output store instructions per wave per block
   extern __shared__ __align__(16) uint16_t lds_h[];
 
   const int unit = blockIdx.x;
@@ -485,16 +484,9 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
   for (int b = 0; b < nb; ++b) {
     const int sl = b % kLinRing;
     const int n = min(kLinBlock, T - kLinBlock * b);
-    // this wave's loads of block b have landed (block b + 1's may still fly).
-    // Vector-memory operations retire in issue order, and the output stores of
-    // block b - 1 were issued after block b + 1's loads: when all of them were
-    // issued (block b - 1 was whole), they are left outstanding too.
-    if (b + 1 < nb) {
-      if (b > 0 && kLinBlock * b <= T) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB + OSTORES));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+    // this wave's loads of block b have landed (block b + 1's may still fly)
+    if (b + 1 < nb) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     if (n < kLinBlock) clear_tail(sl, n);
     lds_barrier();  // block b visible to all waves; block b - 1's slot is free
     if (b + kLinRing - 1 < nb) issue(b + kLinRing - 1, (b + kLinRing - 1) % kLinRing);
