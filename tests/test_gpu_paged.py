@@ -162,16 +162,25 @@ def test_append_bit_exact(hy, dtype):
     assert np.array_equal(gu.host(dv), ref.append_kv(vp, vn, lay.block_tables, ctx, cu))
 
 
-@pytest.mark.parametrize("dtype,D,Hq,Hkv,long", [
-    ("bf16", 128, 8, 2, False), ("f32", 64, 4, 4, False), ("bf16", 64, 4, 1, False),
-    ("bf16", 128, 4, 4, False), ("bf16", 128, 16, 2, False), ("bf16", 64, 4, 2, False),
-    ("bf16", 128, 8, 2, True)])
-def test_prefill_two_chunks_matches_oracle(hy, dtype, D, Hq, Hkv, long):
-    """Causal prefill in two chunks: the second attends to the first through the table."""
+CHUNK_CASES = {  # (total context, first chunk) per request
+    "short": ([150, 33, 64], [100, 16, 1]),
+    "long": ([700, 33, 64], [300, 16, 1]),
+    "empty": ([150, 40, 64], [100, 40, 1]),  # request 1 has no new token in the second chunk
+}
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv,case", [
+    ("bf16", 128, 8, 2, "short"), ("f32", 64, 4, 4, "short"), ("bf16", 64, 4, 1, "short"),
+    ("bf16", 128, 4, 4, "short"), ("bf16", 128, 16, 2, "short"), ("bf16", 64, 4, 2, "short"),
+    ("bf16", 128, 8, 2, "long"), ("bf16", 128, 8, 2, "empty"), ("f32", 64, 4, 2, "empty")])
+def test_prefill_two_chunks_matches_oracle(hy, dtype, D, Hq, Hkv, case):
+    """Causal prefill in two chunks: the second attends to the first through the table.
+    In the "empty" case one request brings no new token to the second chunk: its rows of
+    the packed batch are absent and nothing of it may be written."""
     import torch
     rng = np.random.default_rng(305 + D + Hq)
-    total = np.array([700, 33, 64] if long else [150, 33, 64], np.int32)
-    first = np.array([300, 16, 1] if long else [100, 16, 1], np.int32)
+    total = np.array(CHUNK_CASES[case][0], np.int32)
+    first = np.array(CHUNK_CASES[case][1], np.int32)
     lay = synth.paged_layout(rng, total, n_spare=2)
     kp, vp = _poisoned_pools(rng, lay, Hkv, D, dtype, fill_ctx=np.zeros(3, np.int32))
     dkp, dvp = gu.dev(kp), gu.dev(vp)
