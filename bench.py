@@ -39,6 +39,30 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def rocminfo_gfx950():
+    """Compute units and maximum clock of the first gfx950 agent, as rocminfo reports them
+    (run as a child process); None where it cannot be read."""
+    import subprocess
+    try:
+        text = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in text.split("Agent ")[1:]:
+        fields = {}
+        for line in agent.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
+        if fields.get("Name", "").startswith("gfx950"):
+            def num(key):
+                try:
+                    return int(fields.get(key, "").split()[0])
+                except (ValueError, IndexError):
+                    return None
+            return {"compute_units": num("Compute Unit"), "max_clock_mhz": num("Max Clock Freq. (MHz)")}
+    return None
+
+
 # ---------------------------------------------------------------- workload --
 class Workload:
     """Device-resident inputs of the hybrid step (allocated once)."""
@@ -442,6 +466,9 @@ def main():
     }
     roof = dominant_kernel_roofline(wl, max(1, min(args.steps, 3)))
     log(f"dominant kernel: {roof}")
+    out["device"] = {"name": props.gcnArchName, "peaks_used": {"hbm_gbs": HBM_PEAK_GBS,
+                                                                "bf16_mfma_tflops": BF16_PEAK_TFLOPS},
+                     "rocminfo": rocminfo_gfx950()}
     out["roofline"] = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     out["roofline"]["kernel"] = roof["kernel"]
     out["roofline"]["algorithmic_bytes_per_launch"] = roof["algorithmic_bytes_per_launch"]
