@@ -64,18 +64,10 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // X[row0 + s / 4][c(s % 4)] of a row-major bf16 matrix X, lane i gets
 // X[row0 + j][c(i / 4) + i % 4] for j = 0..3: four consecutive rows of one
 // column, i.e. a k-contiguous MFMA operand read from a row-major tile.
-__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)lds));
-  return __builtin_bit_cast(u32x2, r);
-}
-
-// The same transposing read as an opaque instruction: the compiler neither
-// tracks it nor waits for it, so the caller must wait (lds_wait_all) before
-// using the result. For loops that keep global-to-LDS loads in flight, which
-// the compiler would otherwise drain before every transposing read.
+// Issued as an opaque instruction: the compiler neither tracks it nor waits
+// for it, so the caller must wait (lds_wait_all) before using the result. The
+// compiler's own transposing-read intrinsic would drain every global-to-LDS
+// load in flight before each read, which would serialise the kernels' rings.
 __device__ __forceinline__ u32x2 ds_read_tr16_raw(const uint16_t* lds) {
   const uint32_t a = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)lds));
@@ -100,17 +92,6 @@ __device__ __forceinline__ void lds_wait_all(u32x4 (&x)[N]) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]));
 }
 
-// 8 consecutive rows row0 + 8*(l/16) + 0..7 of column col_q(l%16 / 4) + l%4 of
-// a row-major bf16 tile (row stride rs elements) as a 16x16x32 MFMA operand:
-// two transposing reads; col_q is the lane's column base for its l%16 / 4.
-__device__ __forceinline__ u32x4 tr_operand(const uint16_t* tile, int rs, int row0, int col_q) {
-  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-  const uint16_t* p = tile + (row0 + 8 * g + (s >> 2)) * rs + col_q;
-  const u32x2 a = ds_read_tr16(p);
-  const u32x2 b = ds_read_tr16(p + 4 * rs);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // acc + a.lo * b.lo + a.hi * b.hi for bf16 pairs, in fp32 (v_dot2c_f32_bf16).
@@ -118,8 +99,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
                                          acc, false);
 }
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Workgroup barrier for LDS hand-offs only: waits for the wave's own LDS
 // operations, then s_barrier. Unlike __syncthreads it has no release fence,
@@ -137,18 +116,5 @@ __device__ __forceinline__ void lds_barrier() {
 // outstanding (expcnt and lgkmcnt left at their maxima): vmcnt is split over
 // bits 3:0 and 15:14.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// compile-time integer as a type, and a loop over 0..N-1 unrolled at compile
-// time (the body receives IntTag<i>)
-template <int V> struct IntTag { static constexpr int value = V; };
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-  if constexpr (I < N) {
-    f(IntTag<I>{});
-    static_for_impl<I + 1, N>(f);
-  }
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 
 }  // namespace hy

@@ -308,20 +308,6 @@ template <int D>
 __device__ __forceinline__ int swz_off(int row, int col, int x) {
   return row * D + 8 * ((col >> 3) ^ x) + (col & 7);
 }
-// 8 consecutive rows 8*(l/16) + 0..7 of column c(l%16 / 4) + l%4 of a
-// swizzled 32-row tile as an MFMA operand (two transposing reads). The
-// source lane (l/16, l%16) addresses row 8*(l/16) + (l%16)/4 (and + 4),
-// column col_src; the row's XOR is the same for + 4 (it ignores bit 2).
-template <int D, bool IS_K>
-__device__ __forceinline__ u32x4 tr_swz(const uint16_t* tile, int col_src) {
-  const int l = threadIdx.x & 63;
-  const int row = 8 * (l >> 4) + ((l & 15) >> 2);
-  const uint16_t* p = tile + swz_off<D>(row, col_src, IS_K ? kswz<D>(row) : vswz<D>(row));
-  const u32x2 a = ds_read_tr16(p);
-  const u32x2 b = ds_read_tr16(p + 4 * D);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
