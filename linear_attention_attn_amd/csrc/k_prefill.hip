@@ -24,7 +24,10 @@ constexpr float kMinusHuge = -0x1p100f;    // finite stand-in for -inf as a soft
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
-constexpr int kPrefillNR = 2;    // 16-row tiles per wave
+// 16-row tiles per wave: three (48 rows) amortise each K/V stage, its barrier
+// and its LDS reads over 1.5x the MFMA work of two, and still fit two waves
+// per SIMD (256 VGPRs); four need a whole SIMD per wave and run slower
+constexpr int kPrefillNR = 3;
 
 // ============================================================================
 // Causal prefill, bf16 (MFMA, FlashAttention-style). 1-D grid over (query
@@ -104,7 +107,7 @@ template <> __device__ __forceinline__ void tr_block<64>(const uint32_t (&a)[4],
 }
 
 template <int D, int G, int NR>
-__global__ __launch_bounds__(256) void k_paged_prefill_bf16(
+__global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
     int max_blocks, const int32_t* __restrict__ ctx, const int32_t* __restrict__ cu_q, int H_q,
@@ -275,8 +278,9 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
   // V^T rows 16 dt + lr (head dims), keys 8 lg + 0..7: two transposing reads
   // per tile; source lane (lg, lr) addresses key row 8 lg + lr / 4 (+ 4),
   // head dims 16 dt + 4 (lr % 4) + 0..3 (rows + 4 share the row's XOR). The
-  // reads are requested right after the scores (tr_block), so they complete
-  // while the softmax runs; one explicit wait precedes the products.
+  // reads go out as one opaque block (tr_block) after the softmax (with three
+  // row tiles per wave, fragments requested before it would not fit the
+  // registers); one explicit wait precedes the products.
   auto pv_load = [&](const uint16_t* Vb, u32x4 (&vf)[NDT]) {
     const int vrow = 8 * lg + (lr >> 2);
     uint32_t a[NDT];
@@ -311,8 +315,6 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     u32x4 pb[NR];
     float ps[NR];
     scores(Kb, sc);
-    u32x4 vf[NDT];
-    pv_load(Vb, vf);
     if constexpr (decltype(diag)::value) mask(st * KT, sc);
     bool over = false;
 #pragma unroll
@@ -348,6 +350,8 @@ __global__ __launch_bounds__(256) void k_paged_prefill_bf16(
     }
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) l_run[rt] += ps[rt];
+    u32x4 vf[NDT];
+    pv_load(Vb, vf);
     pv_acc(vf, pb);
   };
 
