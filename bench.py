@@ -12,6 +12,10 @@ tokens served per second (65 536 prefill + 240 decode tokens per step).
 Printed: one JSON line (see the keys below), with the roofline of the dominant
 kernel (paged decode, HBM-bound; HIP events around each of its launches) and
 the fp64 oracle's throughput on a bounded sample of the same workload.
+
+`--kernel-workloads` instead times each layer operation on a workload of its own
+(linear decode batch, linear chunked prefill, paged decode) and prints one JSON
+line per workload; see kernel_workloads().
 """
 from __future__ import annotations
 
@@ -295,6 +299,154 @@ def copy_probe(reps=3):
                       "reps": reps}), flush=True)
 
 
+def kernel_workloads():
+    """Each layer operation on a workload of its own, HIP events on torch's stream, one
+    JSON line per workload (not the bench line):
+      * linear decode: B = 64, H = 32, D = 128, 256 steps from prior states ~ N(0, 0.1);
+        cold steps (a 1 GiB write between steps, untimed, evicts the 134 MB of state from
+        L2 and the MALL) and the mean over 256 back-to-back steps;
+      * linear chunked prefill: 8 requests x 8192 tokens from a zeroed state (zeroed
+        again before every call, untimed), chunk sizes 64, 128 and 256: the first (cold)
+        call, then the median of 10 after 3 warm-ups;
+      * paged decode: B = 128, H_q = 32, H_kv = 8, D = 128, contexts uniform in
+        [512, 32768], 16-token blocks in a permuted pool with 1024 NaN spare blocks:
+        median of 20 after 5 warm-ups.
+    A GPU-side sleep ahead of each timed call lets the host enqueue the events and the
+    launch before the GPU reaches them, so host launch latency is not timed."""
+    import torch
+    from linear_attention_attn_amd import hyattn as hy
+    hy.load()
+    st = torch.cuda.current_stream()
+    dev = "cuda"
+
+    def timed(fn, before=None):
+        if before is not None:
+            before()
+        torch.cuda._sleep(200_000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    # ---- linear decode ----
+    cfg = synth.WORKLOADS["linear_decode"]
+    B, H, D, steps = cfg["B"], cfg["H"], cfg["D"], cfg["steps"]
+    nbytes = hy.hyattn_state_pool_bytes(1, B, H, D)
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    pool = hy.hyattn_state_pool_create(buf, nbytes, 1, B, H, D)
+    sl = torch.tensor(hy.hyattn_state_pool_alloc(pool, B), dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg["seed"])
+    buf.normal_(0.0, cfg["state_scale"], generator=g)
+    qkv = synth.device_normal_bf16((steps, 3, B, H, D), D ** -0.5, cfg["seed"] * 1000 + 1)
+    out = torch.empty(steps, B, H, D, dtype=torch.bfloat16, device=dev)
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    step_bytes = B * H * (2 * D * D * 4 + 4 * D * 2)
+    call = lambda t: hy.hyattn_linear_decode(pool, 0, qkv[t, 0], qkv[t, 1], qkv[t, 2], out[t],
+                                             sl, B, hy.BF16)
+    call(0)
+    torch.cuda.synchronize()
+    cold = [timed(lambda t=t: call(t), before=lambda t=t: scrub.fill_(float(t)))
+            for t in range(steps)]
+    torch.cuda._sleep(200_000)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for t in range(steps):
+        call(t)
+    e1.record(st)
+    e1.synchronize()
+    warm = e0.elapsed_time(e1) / steps
+    tc = float(np.median(cold))
+    emit({"kernel_workload": "linear_decode", "shape": f"B={B} H={H} D={D} bf16 io, fp32 state",
+          "steps": steps, "bytes_per_step": step_bytes,
+          "cold_ms_median": round(tc, 5), "cold_tokens_per_s": round(B * steps / (sum(cold) * 1e-3), 1),
+          "cold_gbs": round(step_bytes / (tc * 1e-3) / 1e9, 1),
+          "cold_hbm_frac": round(step_bytes / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+          "back_to_back_ms": round(warm, 5),
+          "back_to_back_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1)})
+    hy.hyattn_state_pool_destroy(pool)
+    del buf, qkv, out, scrub
+
+    # ---- linear chunked prefill ----
+    cfg = synth.WORKLOADS["linear_prefill"]
+    B, H, D, T = cfg["B"], cfg["H"], cfg["D"], cfg["T"]
+    N = B * T
+    q, k, v = (synth.device_normal_bf16((N, H, D), D ** -0.5, cfg["seed"] * 1000 + i)
+               for i in range(3))
+    o = torch.empty_like(q)
+    cu = torch.as_tensor(synth.cu_lens([T] * B)).to(dev)
+    nbytes = hy.hyattn_state_pool_bytes(1, B, H, D)
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    pool = hy.hyattn_state_pool_create(buf, nbytes, 1, B, H, D)
+    sl = torch.tensor(hy.hyattn_state_pool_alloc(pool, B), dtype=torch.int32, device=dev)
+    pf_bytes = N * H * D * 2 * 4 + 2 * B * H * D * D * 4
+    zero = lambda: hy.hyattn_state_pool_zero(pool, sl, B)
+    calls = {C: (lambda C=C: hy.hyattn_linear_prefill_chunked(pool, 0, q, k, v, o, cu, sl, B, C,
+                                                              hy.BF16))
+             for C in cfg["chunks"]}
+    first = {C: timed(fn, before=zero) for C, fn in calls.items()}
+    for _ in range(3):
+        for fn in calls.values():
+            timed(fn, before=zero)
+    # the chunk sizes take turns, so that clock drift over the run favours none of them
+    reps = {C: [] for C in calls}
+    for _ in range(10):
+        for C, fn in calls.items():
+            reps[C].append(timed(fn, before=zero))
+    for C in cfg["chunks"]:
+        t = float(np.median(reps[C]))
+        # the chunk-size count of the method (Q.S, S update, causal pairs inside each
+        # chunk) and the kernel's own count (32-token blocks whatever the chunk size)
+        flops_c = N * H * (4 * D * D + 2 * (C + 1) * D)
+        flops_k = N * H * (4 * D * D + 2 * 33 * D)
+        t_roof = max(pf_bytes / (HBM_PEAK_GBS * 1e9), flops_k / (BF16_PEAK_TFLOPS * 1e12))
+        emit({"kernel_workload": "linear_prefill", "shape": f"{B}x{T} tokens H={H} D={D} bf16 io",
+              "chunk": C, "first_call_ms": round(first[C], 4), "ms_median": round(t, 4),
+              "tokens_per_s": round(N / (t * 1e-3), 1), "bytes": pf_bytes,
+              "hbm_frac": round(pf_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+              "flops_chunk_count": flops_c,
+              "mfma_frac_chunk_count": round(flops_c / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+              "flops_kernel_count": flops_k,
+              "attainable_roof_frac": round(t_roof / (t * 1e-3), 4)})
+    hy.hyattn_state_pool_destroy(pool)
+    del buf, q, k, v, o
+
+    # ---- paged decode ----
+    cfg = synth.WORKLOADS["paged_decode"]
+    B, Hq, Hkv, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    rng = np.random.default_rng(cfg["seed"])
+    ctx = synth.uniform_contexts(rng, B, cfg["ctx_lo"], cfg["ctx_hi"])
+    lay = synth.paged_layout(rng, ctx, n_spare=cfg["n_spare"])
+    kp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, cfg["seed"] * 1000 + 1)
+    vp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, cfg["seed"] * 1000 + 2)
+    spare = torch.as_tensor(lay.spare.astype(np.int64)).to(dev)
+    kp[spare] = float("nan")
+    vp[spare] = float("nan")
+    q = synth.device_normal_bf16((B, Hq, D), 1.0, cfg["seed"] * 1000 + 3)
+    o = torch.empty_like(q)
+    maxc = int(ctx.max())
+    wsb = hy.hyattn_paged_decode_workspace_bytes(B, Hq, D, maxc)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    bt = torch.as_tensor(lay.block_tables).to(dev)
+    ctx_d = torch.as_tensor(ctx).to(dev)
+    call = lambda: hy.hyattn_paged_decode(q, o, kp, vp, lay.n_blocks, bt, lay.max_blocks, ctx_d,
+                                          maxc, B, Hq, Hkv, D, D ** -0.5, ws, wsb, hy.BF16)
+    for _ in range(5):
+        timed(call)
+    t = float(np.median([timed(call) for _ in range(20)]))
+    kv_bytes = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    emit({"kernel_workload": "paged_decode", "shape": f"B={B} H_q={Hq} H_kv={Hkv} D={D} bf16 KV, "
+          f"contexts uniform in [{cfg['ctx_lo']}, {cfg['ctx_hi']}]",
+          "ms_median": round(t, 4), "tokens_per_s": round(B / (t * 1e-3), 1),
+          "kv_bytes": kv_bytes, "gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
+          "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+
+
 def dominant_kernel_roofline(wl, steps):
     """Average paged-decode launch time over all full layers of `steps` steps."""
     import torch
@@ -411,6 +563,8 @@ def main():
                     help="scale of the longest decode context (1.0 = 131072)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 2 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--kernel-workloads", action="store_true",
+                    help="only time each layer operation on its own workload (one JSON line each)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
@@ -420,6 +574,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
         copy_probe()
+        return
+    if args.kernel_workloads:
+        kernel_workloads()
         return
     from linear_attention_attn_amd import hyattn as hy
     hy.load()

@@ -39,7 +39,9 @@ struct DecodePlan {
   int part_blocks;  // 16-token blocks per context partition
   int max_parts;    // partitions of the longest context
 };
-DecodePlan decode_plan(int max_context);
+// work_pairs = B x H_kv of the launch (0: no floor, the most partitions, which
+// sizes the workspace)
+DecodePlan decode_plan(int max_context, int64_t work_pairs);
 size_t decode_workspace_bytes(int B, int H_q, int D, int max_context);
 
 hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,

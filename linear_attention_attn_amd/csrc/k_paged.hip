@@ -77,17 +77,30 @@ hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_poo
 
 // ============================================================================
 // Decode planning: a request's context is split into partitions of
-// part_blocks blocks (a multiple of 16 blocks = one pass of a workgroup, at
+// part_blocks blocks (a multiple of 4 blocks = one pass of a workgroup, at
 // most kMaxParts partitions for the longest context). Work items are the
 // (request, partition) pairs; k_decode_plan lays them out with an exclusive
 // scan, so the attention grid never holds empty workgroups.
+//
+// Each item starts its waves' load rings from empty and ends with a merge, so
+// long partitions stream better: with work to spare, partitions are at least
+// kPartFloor blocks (4096 tokens). The floor comes down when the work bound
+// (B x H_kv x the longest context's blocks) would leave fewer than about
+// kTargetItems items, so that a small batch still spreads over the chip.
 // ============================================================================
 constexpr int kPassBlocks = 4;  // blocks per workgroup step (4 waves x 1 block)
 constexpr int kMaxParts = 64;
+constexpr int kPartFloor = 256;
+constexpr int64_t kTargetItems = 8192;
 
-DecodePlan decode_plan(int max_context) {
+DecodePlan decode_plan(int max_context, int64_t work_pairs) {
   const int nblk = (max_context + kBlock - 1) / kBlock;
   int pb = (nblk + kMaxParts - 1) / kMaxParts;
+  if (work_pairs > 0) {
+    const int64_t fit = (work_pairs * nblk) / kTargetItems;
+    const int floor_pb = (int)(fit < kPartFloor ? fit : kPartFloor);
+    if (floor_pb > pb) pb = floor_pb;
+  }
   pb = ((pb + kPassBlocks - 1) / kPassBlocks) * kPassBlocks;
   if (pb < kPassBlocks) pb = kPassBlocks;
   int parts = (nblk + pb - 1) / pb;
@@ -101,7 +114,7 @@ static size_t decode_partials_bytes(int B, int H_q, int D, int max_parts) {
 }
 
 size_t decode_workspace_bytes(int B, int H_q, int D, int max_context) {
-  const DecodePlan p = decode_plan(max_context);
+  const DecodePlan p = decode_plan(max_context, 0);  // the most partitions any launch uses
   return decode_partials_bytes(B, H_q, D, p.max_parts) + ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
 }
 
@@ -542,7 +555,7 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
     return launch_simple<64, float>(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, nullptr, 1, B, H_q,
                                     H_kv, sl2, s);
   }
-  const DecodePlan plan = decode_plan(max_context);
+  const DecodePlan plan = decode_plan(max_context, (int64_t)B * H_kv);
   const int G = H_q / H_kv;
   float* ws = (float*)workspace;
   int32_t* cu_parts = reinterpret_cast<int32_t*>(
