@@ -525,6 +525,7 @@ def cpu_baseline(wl):
                             D ** -0.5, threads=threads)
         t_pd += time.time() - t0
         keys += n * H
+        qq1, kk1, vv1, n1, nb1 = qq, kk, vv, n, nb
     rates["paged_decode_head_keys_per_s"] = keys / t_pd
     # (4) causal prefill: the first 512 queries of request 0, `threads` heads
     nq, nh = 512, min(threads, H)
@@ -535,13 +536,44 @@ def cpu_baseline(wl):
     ref.paged_attention(qq, kk, vv, np.arange(nq // 16, dtype=np.int32)[None], [nq], [0, nq],
                         D ** -0.5, units=[(0, h) for h in range(nh)], threads=threads)
     rates["paged_prefill_head_pairs_per_s"] = nh * nq * (nq + 1) // 2 / (time.time() - t0)
+    # the same four operations on one host thread, on smaller samples
+    one = {}
+    t0 = time.time()
+    ref.linear_prefill(q, k, v, [0, P], np.zeros((1, H, D, D)), chunk=C, units=[(0, 0)], threads=1)
+    one["linear_prefill_units_per_s"] = 1 / (time.time() - t0)
+    t0 = time.time()
+    ref.linear_decode(qd[:8], kd[:8], vd[:8], std[:8].copy(), threads=1)
+    one["linear_decode_units_per_s"] = 8 * H / (time.time() - t0)
+    t0 = time.time()
+    ref.paged_attention(qq1, kk1, vv1, np.arange(nb1, dtype=np.int32)[None], [n1], [0, 1],
+                        D ** -0.5, threads=1)
+    one["paged_decode_head_keys_per_s"] = n1 * H / (time.time() - t0)
+    t0 = time.time()
+    ref.paged_attention(qq, kk, vv, np.arange(nq // 16, dtype=np.int32)[None], [nq], [0, nq],
+                        D ** -0.5, units=[(0, 0)], threads=1)
+    one["paged_prefill_head_pairs_per_s"] = nq * (nq + 1) // 2 / (time.time() - t0)
+
     # extrapolate one whole step
     dec_keys = int(wl.ctx[wl.n_p:].astype(np.int64).sum())
-    step_s = (wl.n_lin * (wl.n_p * H / rates["linear_prefill_units_per_s"]
-                          + wl.n_d * H / rates["linear_decode_units_per_s"])
-              + wl.n_full * (H * dec_keys / rates["paged_decode_head_keys_per_s"]
-                             + wl.n_p * H * (P * (P + 1) // 2) / rates["paged_prefill_head_pairs_per_s"]))
+
+    def step_seconds(rt):
+        return (wl.n_lin * (wl.n_p * H / rt["linear_prefill_units_per_s"]
+                            + wl.n_d * H / rt["linear_decode_units_per_s"])
+                + wl.n_full * (H * dec_keys / rt["paged_decode_head_keys_per_s"]
+                               + wl.n_p * H * (P * (P + 1) // 2) / rt["paged_prefill_head_pairs_per_s"]))
+    step_s = step_seconds(rates)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=round(wl.tokens / step_s, 3), unit="tokens/s", cores=threads, kind="oracle",
+                cpu_model=cpu_model,
+                one_thread={"value": round(wl.tokens / step_seconds(one), 4), "unit": "tokens/s",
+                            "sample": "1 linear-prefill unit, 8 x 32 linear-decode units, the last "
+                                      "sampled paged-decode request, 512-query causal prefill x 1 head",
+                            "rates": {k: round(x, 2) for k, x in one.items()}},
                 sample=(f"fp64 oracle, {threads} threads, on sampled units of the same step: "
                         f"{nu} linear-prefill (request, head) units of 4096 tokens, {nr * H} "
                         "linear-decode units, 4 paged-decode requests (all heads and keys), "
