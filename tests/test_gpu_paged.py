@@ -92,6 +92,25 @@ def test_decode_many_partitions(hy):
     gu.assert_bf16(got, want, "paged decode, long contexts")
 
 
+def test_decode_work_scaled_partitions(hy):
+    """A batch whose partition size comes from the work bound rather than from the longest
+    context alone: B = 24 x H_kv = 8 pairs x 2000 blocks leaves 48-block partitions (the
+    longest context alone would give 32, the floor's cap is 256). Sampled requests against
+    the oracle."""
+    rng = np.random.default_rng(302)
+    D, Hq, Hkv = 128, 32, 8
+    ctx = synth.uniform_contexts(rng, 24, 512, 32000)
+    ctx[int(np.argmax(ctx))] = 32000
+    lay = synth.paged_layout(rng, ctx, n_spare=2)
+    kp, vp = _poisoned_pools(rng, lay, Hkv, D, "bf16")
+    q = synth.normal(rng, (len(ctx), Hq, D), 1.0, "bf16")
+    got = _decode(hy, q, kp, vp, lay, Hq, Hkv, D, D ** -0.5, "bf16")
+    samp = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 3, 17})
+    want = ref.paged_attention(q[samp], kp, vp, lay.block_tables[samp], ctx[samp],
+                               np.arange(len(samp) + 1), D ** -0.5)
+    gu.assert_bf16(got[samp], want, "paged decode, work-scaled partitions")
+
+
 def test_decode_onehot_probe_bit_exact(hy):
     """q = 64 e0 against one key 64 e0 (others 0): the output is that token's value, exactly.
 
