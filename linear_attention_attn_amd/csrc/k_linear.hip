@@ -44,12 +44,22 @@ hipError_t launch_state_zero(float* pool, int n_layers, int n_slots, int64_t slo
 }
 
 // ============================================================================
-// Decode: one workgroup per (request, head). S streams through registers once:
-// each thread owns 4 adjacent columns of D/RG rows; it adds k[i] v[j], then
-// accumulates q[i] S_new[i][j]. The per-thread partial outputs are summed over
-// the row groups in LDS in a fixed order (deterministic).
+// Decode: one workgroup per (request, head) and column slice. S streams
+// through registers once: with NCS slices of D / NCS value columns, each
+// thread owns 4 adjacent columns of D / RG rows of its slice; it adds
+// k[i] v[j], then accumulates q[i] S_new[i][j]. The per-thread partial
+// outputs are summed over the row groups in LDS in a fixed order
+// (deterministic); a slice's output columns need no other slice.
+// Large batches take NCS = 4: four times the workgroups, each a quarter of a
+// state, which evens out the last round over the CUs (3.7 % faster at 7 680
+// (request, head) units); small batches keep whole states per workgroup
+// (NCS = 1), for which the split was 6 % slower at 2 048 units.
+// XCD-major order: workgroup ids go round-robin over the 8 XCDs, and XCD x
+// (ids x, x + 8, ...) takes the consecutive items x P .. x P + P - 1, so each
+// XCD streams one contiguous eighth of the listed states. The grid has 8 P ids
+// (P = ceil(items / 8)); ids past the last item exit.
 // ============================================================================
-template <int D, typename T, bool GATED>
+template <int D, typename T, bool GATED, int NCS>
 __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ states, int n_slots,
                                                        const T* __restrict__ q,
                                                        const T* __restrict__ k,
@@ -57,24 +67,24 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
                                                        const float* __restrict__ log_gamma,
                                                        const int32_t* __restrict__ slots, int H,
                                                        int n_units) {
-  constexpr int C4 = D / 4;      // threads across a row (4 floats each)
+  constexpr int DC = D / NCS;    // value columns of this workgroup
+  constexpr int C4 = DC / 4;     // threads across a row (4 floats each)
   constexpr int RG = 256 / C4;   // row groups
   constexpr int RP = D / RG;     // rows per thread
-  __shared__ float sq[D], sk[D], sv[D];
-  __shared__ float red[RG][D];
+  static_assert(RP >= 1 && RG * RP == D, "k_linear_decode: column split does not tile D");
+  __shared__ float sq[D], sk[D], sv[DC];
+  __shared__ float red[RG][DC];
 
-  // XCD-major order: workgroup ids go round-robin over the 8 XCDs, and XCD x
-  // (ids x, x + 8, ...) takes the consecutive units x P .. x P + P - 1, so
-  // each XCD streams one contiguous eighth of the listed states. The grid has
-  // 8 P ids (P = ceil(n_units / 8)); ids past the last unit exit.
   const int per = (int)gridDim.x >> 3;
-  const int unit = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);  // r * H + h
-  if (unit >= n_units) return;
+  const int item = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  if (item >= n_units * NCS) return;
+  const int unit = item / NCS;            // r * H + h
+  const int col0 = (item - unit * NCS) * DC;
   const int r = unit / H;
   const int h = unit - r * H;
   const int slot = slots[r];
   if (slot < 0 || slot >= n_slots) return;
-  float* S = states + ((int64_t)slot * H + h) * (int64_t)(D * D);
+  float* S = states + ((int64_t)slot * H + h) * (int64_t)(D * D) + col0;
   const int64_t xo = (int64_t)unit * D;
   const int t = threadIdx.x;
   const int c4 = t % C4, rg = t / C4;
@@ -86,8 +96,8 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
   if (t < D) {
     sq[t] = io<T>::ld(q, xo + t);
     sk[t] = io<T>::ld(k, xo + t);
-    sv[t] = io<T>::ld(v, xo + t);
   }
+  if (t < DC) sv[t] = io<T>::ld(v, xo + col0 + t);
   __syncthreads();
 
   const f32x4 vv = {sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]};
@@ -115,28 +125,40 @@ __global__ __launch_bounds__(256) void k_linear_decode(float* __restrict__ state
   red[rg][4 * c4 + 2] = acc[2];
   red[rg][4 * c4 + 3] = acc[3];
   __syncthreads();
-  if (t < D) {
+  if (t < DC) {
     float sum = 0.f;
 #pragma unroll
     for (int g = 0; g < RG; ++g) sum += red[g][t];
-    io<T>::st(o, xo + t, sum);
+    io<T>::st(o, xo + col0 + t, sum);
   }
 }
+
+// (request, head) units from which the decode splits each state over 4 workgroups
+constexpr int64_t kDecodeSplitUnits = 4096;
 
 hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q, const void* k,
                                 const void* v, void* o, const float* log_gamma,
                                 const int32_t* slots, int B, int H, int D, bool bf16,
                                 hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  dim3 grid((unsigned)(8 * ((B * H + 7) / 8))), block(256);
-#define HY_DEC(DD, TT, GG)                                                                    \
-  hipLaunchKernelGGL((k_linear_decode<DD, TT, GG>), grid, block, 0, s, layer_states, n_slots, \
+  const bool split = (int64_t)B * H >= kDecodeSplitUnits;
+  dim3 grid((unsigned)(8 * (((int64_t)B * H * (split ? 4 : 1) + 7) / 8))), block(256);
+#define HY_DEC_N(DD, TT, GG, NN)                                                                   \
+  hipLaunchKernelGGL((k_linear_decode<DD, TT, GG, NN>), grid, block, 0, s, layer_states, n_slots, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, log_gamma, slots, H, B * H)
-#define HY_DEC_G(DD, TT)       \
-  if (log_gamma)               \
-    HY_DEC(DD, TT, true);      \
-  else                         \
-    HY_DEC(DD, TT, false)
+#define HY_DEC(DD, TT, GG)            \
+  if (split)                          \
+    HY_DEC_N(DD, TT, GG, 4);          \
+  else                                \
+    HY_DEC_N(DD, TT, GG, 1)
+#define HY_DEC_G(DD, TT)         \
+  do {                           \
+    if (log_gamma) {             \
+      HY_DEC(DD, TT, true);      \
+    } else {                     \
+      HY_DEC(DD, TT, false);     \
+    }                            \
+  } while (0)
   if (D == 128) {
     if (bf16) HY_DEC_G(128, uint16_t); else HY_DEC_G(128, float);
   } else {
@@ -144,6 +166,7 @@ hipError_t launch_linear_decode(float* layer_states, int n_slots, const void* q,
   }
 #undef HY_DEC_G
 #undef HY_DEC
+#undef HY_DEC_N
   return hipGetLastError();
 }
 

@@ -127,6 +127,45 @@ def test_gated_decode_matches_oracle(hy, dtype, D):
     pool.close()
 
 
+@pytest.mark.parametrize("gated,dtype,D", [(False, "bf16", 128), (True, "bf16", 128),
+                                           (True, "f32", 64)])
+def test_decode_large_batch(hy, gated, dtype, D):
+    """B x H = 4352 (request, head) units: the decode splits each state over 4 workgroups
+    (column slices) from 4096 units on. Sampled units against the oracle, outputs and
+    states."""
+    import torch
+    rng = np.random.default_rng(410 + D + int(gated))
+    B, H = 136, 32
+    pool = Pool(hy, 1, B, H, D)
+    slots = pool.alloc(B)[::-1]
+    g0 = torch.Generator(device="cuda")
+    g0.manual_seed(411)
+    pool.view.normal_(0.0, 0.1, generator=g0)
+    units = [(int(r), int(h)) for r, h in zip(rng.integers(0, B, 24), rng.integers(0, H, 24))]
+    units = sorted(set(units))
+    st = np.zeros((B, H, D, D))
+    for r, h in units:
+        st[r, h] = gu.host(pool.view[0, slots[r], h]).astype(np.float64)
+    q, k, v = (synth.normal(rng, (B, H, D), D ** -0.5, dtype) for _ in range(3))
+    g = synth.log_forget(rng, (B, H)) if gated else None
+    dq = gu.dev(q)
+    do = torch.full_like(dq, float("nan"))
+    if gated:
+        hy.hyattn_linear_decode_gated(pool.handle, 0, dq, gu.dev(k), gu.dev(v), gu.dev(g), do,
+                                      gu.i32(slots), B, _dt(hy, dtype))
+    else:
+        hy.hyattn_linear_decode(pool.handle, 0, dq, gu.dev(k), gu.dev(v), do, gu.i32(slots), B,
+                                _dt(hy, dtype))
+    torch.cuda.synchronize()
+    want = ref.linear_decode(q, k, v, st, units=units, log_gamma=g)
+    got = gu.host(do)
+    idx = tuple(np.array(units).T)
+    gu.assert_io(got[idx], want[idx], dtype, "large-batch decode outputs")
+    gu.assert_f32(np.stack([gu.host(pool.view[0, slots[r], h]) for r, h in units]),
+                  np.stack([st[r, h] for r, h in units]), "large-batch decode states")
+    pool.close()
+
+
 def test_zero_gates_reproduce_the_plain_layer_bit_for_bit(hy):
     """g = 0 multiplies by exactly 1 and adds exact zeros (the lo half of the
     weighted values), so the gated kernels must give the plain ones' bits."""
