@@ -196,3 +196,23 @@ def device_log_forget(shape, seed: int, device="cuda"):
     u = torch.rand((N, H), generator=g, device=device, dtype=torch.float64)
     e = 2.0 + (torch.arange(H, device=device, dtype=torch.float64) % 8)
     return torch.log1p(-u * torch.exp2(-e)).clamp(max=0.0).to(torch.float32)
+
+
+def tiny_inputs():
+    """The tiny workload's inputs (WORKLOADS["tiny"]): one request of T + n_decode
+    tokens, seed 0, fp32. The linear layer and the full layer each get their own q, k,
+    v ~ N(0,1) * D^-0.5 of shape [T + n_decode][H][D] (the full layer has H_kv = H).
+    The full layer's pool holds n_blocks 16-token blocks, all NaN at first; the
+    request's blocks come from a seeded permutation of the pool, so its logical blocks
+    are scattered and the blocks it never uses stay NaN."""
+    cfg = WORKLOADS["tiny"]
+    rng = np.random.default_rng(cfg["seed"])
+    H, D, n = cfg["H"], cfg["D"], cfg["T"] + cfg["n_decode"]
+    s = D ** -0.5
+    lin = {x: normal(rng, (n, H, D), s, cfg["dtype"]) for x in ("q", "k", "v")}
+    full = {x: normal(rng, (n, H, D), s, cfg["dtype"]) for x in ("q", "k", "v")}
+    n_used = (n + BLOCK - 1) // BLOCK
+    lay = paged_layout(rng, [n], n_spare=cfg["n_blocks"] - n_used)
+    pool_nan = np.full((lay.n_blocks, H, BLOCK, D), np.nan, np.float32)
+    return dict(cfg=cfg, linear=lin, full=full, layout=lay, k_pool=pool_nan,
+                v_pool=pool_nan.copy())

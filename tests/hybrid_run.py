@@ -11,7 +11,9 @@ from oracle import ref
 from tests import gpu_util as gu
 
 
-def run_gpu(case, slot_perm=None):
+def setup_gpu(case, slot_perm=None):
+    """Device copies of a synth.hybrid case, a state pool with the case's prior
+    states in its slots, and the hyattn_batch of the step. Returns a dict."""
     import torch
     from linear_attention_attn_amd import hyattn as hy
     from linear_attention_attn_amd import layer_types
@@ -33,7 +35,7 @@ def run_gpu(case, slot_perm=None):
     for li in range(n_lin):
         for r in range(B):
             view[li, slots[r]] = torch.from_numpy(case["states"][li, r]).cuda()
-    dev_layers, keep = [], []
+    dev_layers = []
     fi = 0
     for t, io in zip(types, case["layers"]):
         d = {n: gu.dev(io[n]) for n in ("q", "k", "v")}
@@ -49,20 +51,28 @@ def run_gpu(case, slot_perm=None):
     tensors = dict(cu_seqlens=gu.i32(case["prefill_cu"]), prefill_slots=gu.i32(slots[:n_p]),
                    decode_slots=gu.i32(slots[n_p:]), block_tables=gu.i32(lay.block_tables),
                    context_lens=gu.i32(case["ctx"]), cu_q_lens=gu.i32(case["cu_q"]), workspace=ws)
-    batch = hy.make_batch(n_prefill=n_p, n_decode=n_d, n_prefill_tokens=int(case["prefill_cu"][-1]),
-                          max_prefill_len=case["max_prefill_len"],
-                          max_blocks_per_seq=lay.max_blocks, max_context=int(case["ctx"].max()),
-                          n_blocks=lay.n_blocks, H=H, H_kv=Hkv, D=D, chunk_size=case["chunk"],
-                          scale=case["scale"], dtype=hy.BF16 if case["dtype"] == "bf16" else hy.F32,
-                          workspace_bytes=ws_bytes, **tensors)
-    hy.hyattn_hybrid_step(types, len(types), dev_layers, batch, pool)
+    kw = dict(n_prefill=n_p, n_decode=n_d, n_prefill_tokens=int(case["prefill_cu"][-1]),
+              max_prefill_len=case["max_prefill_len"], max_blocks_per_seq=lay.max_blocks,
+              max_context=int(case["ctx"].max()), n_blocks=lay.n_blocks, H=H, H_kv=Hkv, D=D,
+              chunk_size=case["chunk"], scale=case["scale"],
+              dtype=hy.BF16 if case["dtype"] == "bf16" else hy.F32, workspace_bytes=ws_bytes)
+    return dict(hy=hy, types=types, n_lin=n_lin, B=B, buf=buf, view=view, pool=pool, slots=slots,
+                layers=dev_layers, tensors=tensors, batch_kw=kw,
+                batch=hy.make_batch(**kw, **tensors))
+
+
+def run_gpu(case, slot_perm=None):
+    import torch
+    g = setup_gpu(case, slot_perm)
+    hy, types, view, slots, B, n_lin = g["hy"], g["types"], g["view"], g["slots"], g["B"], g["n_lin"]
+    hy.hyattn_hybrid_step(types, len(types), g["layers"], g["batch"], g["pool"])
     torch.cuda.synchronize()
-    outs = [gu.host(d["o"]) for d in dev_layers]
+    outs = [gu.host(d["o"]) for d in g["layers"]]
     states = np.stack([np.stack([gu.host(view[li, slots[r]]) for r in range(B)])
                        for li in range(n_lin)]) if n_lin else None
-    pools = [(gu.host(d["k_pool"]), gu.host(d["v_pool"])) for t, d in zip(types, dev_layers)
+    pools = [(gu.host(d["k_pool"]), gu.host(d["v_pool"])) for t, d in zip(types, g["layers"])
              if t == 1]
-    hy.hyattn_state_pool_destroy(pool)
+    hy.hyattn_state_pool_destroy(g["pool"])
     return outs, states, pools
 
 
@@ -79,11 +89,28 @@ def run_oracle(case, units_linear=None, units_full=None):
 
 
 def compare(case, got, want, check_pools=True):
+    """Outputs against the oracle's (full layers with the softmax-weight rounding term
+    in the bf16 bound, computed over the oracle's pools after append), final states
+    at the fp32 rule, pools bit for bit. A one-step case gives its query offsets as
+    cu_q; a multi-step case is compared with the oracle's single step over all new
+    tokens, whose offsets are its cu."""
     g_outs, g_states, g_pools = got
     w_outs, w_states, w_pools = want
+    lay = case["layout"]
+    ctx = case["ctx"]
+    cu = case["cu_q"] if "cu_q" in case else case["cu"]
     report = []
+    fi = 0
     for i, (g, w) in enumerate(zip(g_outs, w_outs)):
-        report.append((i, case["types"][i], gu.assert_io(g, w, case["dtype"], f"layer {i} output")))
+        delta = None
+        if case["types"][i] == "full":
+            if case["dtype"] == "bf16":
+                q = case["layers"][i]["q"]
+                kp, vp = w_pools[fi]
+                delta = gu.attention_delta(q, kp, vp, lay.block_tables, ctx, cu, case["scale"], w)
+            fi += 1
+        report.append((i, case["types"][i],
+                       gu.assert_io(g, w, case["dtype"], f"layer {i} output", delta)))
     if g_states is not None:
         gu.assert_f32(g_states, w_states, "linear states")
     if check_pools:

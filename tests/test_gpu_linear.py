@@ -178,7 +178,7 @@ def test_chunk_size_invariance_and_continuation(hy):
         outs[chunk] = got
         pool.close()
     for c in (16, 128):
-        gu.assert_bf16(outs[c], gu.as_f64(outs[64]), f"C={c} vs C=64")
+        gu.assert_bf16_pair(outs[c], outs[64], f"C={c} vs C=64")
 
 
 def test_batch_consistency_and_slot_isolation(hy):

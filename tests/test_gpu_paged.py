@@ -74,9 +74,11 @@ def test_decode_matches_oracle(hy, dtype, D, Hq, Hkv):
     q = synth.normal(rng, (len(ctx), Hq, D), 1.0, dtype)
     scale = D ** -0.5
     got = _decode(hy, q, kp, vp, lay, Hq, Hkv, D, scale, dtype)
-    want = ref.paged_attention(q, kp, vp, lay.block_tables, ctx, np.arange(len(ctx) + 1), scale)
+    cu = np.arange(len(ctx) + 1)
+    want = ref.paged_attention(q, kp, vp, lay.block_tables, ctx, cu, scale)
     assert not gu.as_f64(got[0]).any(), "empty context gives zeros"
-    gu.assert_io(got, want, dtype, "paged decode")
+    delta = gu.attention_delta(q, kp, vp, lay.block_tables, ctx, cu, scale, want)
+    gu.assert_io(got, want, dtype, "paged decode", delta)
 
 
 def test_decode_many_partitions(hy):
@@ -88,8 +90,10 @@ def test_decode_many_partitions(hy):
     kp, vp = _poisoned_pools(rng, lay, Hkv, D, "bf16")
     q = synth.normal(rng, (len(ctx), Hq, D), 1.0, "bf16")
     got = _decode(hy, q, kp, vp, lay, Hq, Hkv, D, D ** -0.5, "bf16")
-    want = ref.paged_attention(q, kp, vp, lay.block_tables, ctx, np.arange(len(ctx) + 1), D ** -0.5)
-    gu.assert_bf16(got, want, "paged decode, long contexts")
+    cu = np.arange(len(ctx) + 1)
+    want = ref.paged_attention(q, kp, vp, lay.block_tables, ctx, cu, D ** -0.5)
+    delta = gu.attention_delta(q, kp, vp, lay.block_tables, ctx, cu, D ** -0.5, want)
+    gu.assert_bf16(got, want, "paged decode, long contexts", delta)
 
 
 def test_decode_work_scaled_partitions(hy):
@@ -106,9 +110,11 @@ def test_decode_work_scaled_partitions(hy):
     q = synth.normal(rng, (len(ctx), Hq, D), 1.0, "bf16")
     got = _decode(hy, q, kp, vp, lay, Hq, Hkv, D, D ** -0.5, "bf16")
     samp = sorted({int(np.argmax(ctx)), int(np.argmin(ctx)), 3, 17})
-    want = ref.paged_attention(q[samp], kp, vp, lay.block_tables[samp], ctx[samp],
-                               np.arange(len(samp) + 1), D ** -0.5)
-    gu.assert_bf16(got[samp], want, "paged decode, work-scaled partitions")
+    cu = np.arange(len(samp) + 1)
+    want = ref.paged_attention(q[samp], kp, vp, lay.block_tables[samp], ctx[samp], cu, D ** -0.5)
+    delta = gu.attention_delta(q[samp], kp, vp, lay.block_tables[samp], ctx[samp], cu, D ** -0.5,
+                               want)
+    gu.assert_bf16(got[samp], want, "paged decode, work-scaled partitions", delta)
 
 
 def test_decode_onehot_probe_bit_exact(hy):
@@ -223,7 +229,8 @@ def test_prefill_two_chunks_matches_oracle(hy, dtype, D, Hq, Hkv, case):
         kp_ref = ref.append_kv(kp_ref, kn, lay.block_tables, ctx, cu)
         vp_ref = ref.append_kv(vp_ref, vn, lay.block_tables, ctx, cu)
         want = ref.paged_attention(q, kp_ref, vp_ref, lay.block_tables, ctx, cu, scale)
-        gu.assert_io(gu.host(do), want, dtype, f"paged prefill stage {stage}")
+        delta = gu.attention_delta(q, kp_ref, vp_ref, lay.block_tables, ctx, cu, scale, want)
+        gu.assert_io(gu.host(do), want, dtype, f"paged prefill stage {stage}", delta)
 
 
 def test_checked_mode_rejects_bad_block_ids(hy, monkeypatch):
