@@ -577,6 +577,68 @@ size_t hyattn_hybrid_workspace_bytes(const hyattn_batch* b) {
   return hy::decode_workspace_bytes(b->n_decode, b->H, b->D, b->max_context);
 }
 
+// Checked mode for the hybrid step: every index array of the batch is read once
+// and validated before the step launches anything.
+static hyattn_status check_step_contents(const hyattn_batch* b, hyattn_state_pool* p, int n_lin,
+                                         int n_full, const int32_t* layer_types, int n_layers,
+                                         const hyattn_layer_io* layers, hipStream_t s) {
+  const int B = b->n_prefill + b->n_decode;
+  hyattn_status st;
+  std::vector<int32_t> cu_p;
+  if (b->n_prefill > 0) {
+    if ((st = fetch(cu_p, b->cu_seqlens, (size_t)b->n_prefill + 1, s)) != HYATTN_OK) return st;
+    if ((st = check_cu(cu_p, b->max_prefill_len, "cu_seqlens")) != HYATTN_OK) return st;
+    if (cu_p[b->n_prefill] != b->n_prefill_tokens)
+      return fail(HYATTN_ERR_INVALID_ARG, "cu_seqlens[%d] = %d but n_prefill_tokens = %d",
+                  b->n_prefill, cu_p[b->n_prefill], b->n_prefill_tokens);
+  }
+  if (n_lin > 0) {
+    // prefill and decode slots together: allocated, zeroed since allocation, no repeats
+    std::vector<int32_t> sp, sd;
+    if (b->n_prefill > 0 && (st = fetch(sp, b->prefill_slots, (size_t)b->n_prefill, s)) != HYATTN_OK)
+      return st;
+    if (b->n_decode > 0 && (st = fetch(sd, b->decode_slots, (size_t)b->n_decode, s)) != HYATTN_OK)
+      return st;
+    sp.insert(sp.end(), sd.begin(), sd.end());
+    std::lock_guard<std::mutex> lk(p->mu);
+    std::vector<unsigned char> seen(p->n_slots, 0);
+    for (size_t i = 0; i < sp.size(); ++i) {
+      const int id = sp[i];
+      if (id < 0 || id >= p->n_slots)
+        return fail(HYATTN_ERR_BAD_SLOT, "slot %d (request %zu) outside [0, %d)", id, i, p->n_slots);
+      if (!p->used[id]) return fail(HYATTN_ERR_BAD_SLOT, "slot %d (request %zu) is not allocated", id, i);
+      if (!p->zeroed[id])
+        return fail(HYATTN_ERR_BAD_SLOT, "slot %d (request %zu) was never zeroed since allocation", id, i);
+      if (seen[id]) return fail(HYATTN_ERR_INVALID_ARG, "slot %d serves two requests of the step", id);
+      seen[id] = 1;
+    }
+  }
+  for (int i = 0; i < n_layers; ++i)
+    if (layer_types[i] == HYATTN_LAYER_LINEAR && layers[i].log_gamma &&
+        (st = check_log_gamma(layers[i].log_gamma,
+                              ((size_t)(b->n_prefill > 0 ? b->n_prefill_tokens : 0) + b->n_decode) * b->H,
+                              s)) != HYATTN_OK)
+      return st;
+  if (n_full > 0) {
+    std::vector<int32_t> cu_q, c;
+    if ((st = fetch(cu_q, b->cu_q_lens, (size_t)B + 1, s)) != HYATTN_OK) return st;
+    for (int r = 0; r <= B; ++r) {  // cu_seqlens, then one row per decode request
+      const int want = r <= b->n_prefill ? (b->n_prefill > 0 ? cu_p[r] : 0)
+                                         : (b->n_prefill > 0 ? cu_p[b->n_prefill] : 0) + r - b->n_prefill;
+      if (cu_q[r] != want)
+        return fail(HYATTN_ERR_INVALID_ARG, "cu_q_lens[%d] = %d, expected %d", r, cu_q[r], want);
+    }
+    if ((st = check_tables(b->block_tables, B, b->max_blocks_per_seq, b->context_lens,
+                           b->max_context, b->n_blocks, s, &c)) != HYATTN_OK)
+      return st;
+    for (int r = 0; r < B; ++r)
+      if (cu_q[r + 1] - cu_q[r] > c[r])
+        return fail(HYATTN_ERR_INVALID_ARG, "request %d: %d new tokens > context %d", r,
+                    cu_q[r + 1] - cu_q[r], c[r]);
+  }
+  return ok();
+}
+
 hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
                                  const hyattn_layer_io* layers, const hyattn_batch* b,
                                  hyattn_state_pool* p, void* stream) {
@@ -595,11 +657,18 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
       return fail(HYATTN_ERR_UNSUPPORTED_LAYER, "layer %d: attention type %d is not supported", i,
                   layer_types[i]);
   }
-  // 2. batch and per-layer arguments, before any launch
+  // 2. every argument of every layer, before any launch: a step that fails has
+  //    no side effects (no linear state advanced, no token appended)
   if (b->n_prefill < 0 || b->n_decode < 0)
     return fail(HYATTN_ERR_INVALID_ARG, "negative request counts");
   const int B = b->n_prefill + b->n_decode;
   if (!dtype_ok(b->dtype)) return fail(HYATTN_ERR_UNSUPPORTED, "dtype %d not supported", b->dtype);
+  if (b->n_prefill > 0) {
+    if (!b->cu_seqlens) return fail(HYATTN_ERR_INVALID_ARG, "prefill requests need cu_seqlens");
+    if (b->n_prefill_tokens < 0 || b->max_prefill_len < 0)
+      return fail(HYATTN_ERR_INVALID_ARG, "n_prefill_tokens and max_prefill_len must be >= 0");
+  }
+  const bool bf16 = b->dtype == HYATTN_BF16;
   if (n_lin > 0) {
     if (!p) return fail(HYATTN_ERR_INVALID_ARG, "linear layers need a state pool");
     if (n_lin > p->n_layers)
@@ -608,8 +677,8 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
     if (p->H != b->H || p->D != b->D)
       return fail(HYATTN_ERR_INVALID_ARG, "pool (H=%d, D=%d) does not match batch (H=%d, D=%d)",
                   p->H, p->D, b->H, b->D);
-    if (b->n_prefill > 0 && (!b->cu_seqlens || !b->prefill_slots))
-      return fail(HYATTN_ERR_INVALID_ARG, "prefill requests need cu_seqlens and slots");
+    if (b->n_prefill > 0 && !b->prefill_slots)
+      return fail(HYATTN_ERR_INVALID_ARG, "prefill requests need slots");
     if (b->n_decode > 0 && !b->decode_slots)
       return fail(HYATTN_ERR_INVALID_ARG, "decode requests need slots");
     bool any_gated = false;
@@ -624,9 +693,15 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
     if (st != HYATTN_OK) return st;
     if (!b->block_tables || !b->context_lens || !b->cu_q_lens)
       return fail(HYATTN_ERR_INVALID_ARG, "full layers need block tables, context and q lengths");
+    if (b->max_context < 0 || (int64_t)b->max_context > (int64_t)b->max_blocks_per_seq * 16)
+      return fail(HYATTN_ERR_INVALID_ARG, "max_context %d outside [0, 16 * max_blocks_per_seq]",
+                  b->max_context);
+    const int G = b->H / b->H_kv;
+    if (bf16 && G != 1 && G != 2 && G != 4 && G != 8)
+      return fail(HYATTN_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", G);
     if (b->n_decode > 0) {
       const size_t need = hy::decode_workspace_bytes(b->n_decode, b->H, b->D, b->max_context);
-      if (b->dtype == HYATTN_BF16 && (!b->workspace || b->workspace_bytes < need))
+      if (bf16 && (!b->workspace || b->workspace_bytes < need))
         return fail(HYATTN_ERR_INVALID_ARG, "workspace needs %zu bytes", need);
     }
   }
@@ -639,65 +714,57 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
     if (layer_types[i] == HYATTN_LAYER_FULL && L.log_gamma)
       return fail(HYATTN_ERR_INVALID_ARG, "layer %d: log_gamma is for linear layers only", i);
   }
+  if (B == 0) return ok();
+  hipStream_t s = as_stream(stream);
+  if (checked_mode()) {
+    hyattn_status st = check_step_contents(b, p, n_lin, n_full, layer_types, n_layers, layers, s);
+    if (st != HYATTN_OK) return st;
+  }
   if (getenv("HYATTN_LOG")) {
     std::string plan;
     for (int i = 0; i < n_layers; ++i) plan += layer_types[i] == HYATTN_LAYER_LINEAR ? 'L' : 'F';
     fprintf(stderr, "[hyattn] step: %d layers (%d linear, %d full) plan %s; %d prefill + %d decode\n",
             n_layers, n_lin, n_full, plan.c_str(), b->n_prefill, b->n_decode);
   }
-  hipStream_t s = as_stream(stream);
-  const size_t esz = b->dtype == HYATTN_BF16 ? 2 : 4;
-  hyattn_status st = ok();
-  // 3. launches in layer order
-  if (B == 0) return ok();
+  // 3. launches in layer order (arguments validated above)
+  const size_t esz = bf16 ? 2 : 4;
   const int n_prefill_tok = b->n_prefill > 0 ? b->n_prefill_tokens : 0;
-  if (n_prefill_tok < 0) return fail(HYATTN_ERR_INVALID_ARG, "n_prefill_tokens < 0");
-  const size_t row_h = (size_t)b->H * b->D * esz;
+  const size_t off = (size_t)n_prefill_tok * b->H * b->D * esz;  // first decode row
+  const int max_q_len = b->n_prefill > 0 ? std::max(b->max_prefill_len, 1) : 1;
   int li = 0;
   for (int i = 0; i < n_layers; ++i) {
     const hyattn_layer_io& L = layers[i];
+    hipError_t e = hipSuccess;
     if (layer_types[i] == HYATTN_LAYER_LINEAR) {
-      const bool gated = L.log_gamma != nullptr;
-      if (b->n_prefill > 0) {
-        st = linear_prefill(p, li, L.q, L.k, L.v, L.log_gamma, L.o, b->cu_seqlens,
-                            b->prefill_slots, b->n_prefill, b->chunk_size, b->dtype, stream,
-                            gated);
-        if (st != HYATTN_OK) return st;
-      }
-      if (b->n_decode > 0) {
-        const size_t off = (size_t)n_prefill_tok * row_h;
-        st = linear_decode(p, li, (const char*)L.q + off, (const char*)L.k + off,
-                           (const char*)L.v + off,
-                           gated ? L.log_gamma + (size_t)n_prefill_tok * b->H : nullptr,
-                           (char*)L.o + off, b->decode_slots, b->n_decode, b->dtype, stream,
-                           gated);
-        if (st != HYATTN_OK) return st;
-      }
-      ++li;
+      float* base = layer_base(p, li++);
+      if (b->n_prefill > 0)
+        e = hy::launch_linear_prefill(base, p->n_slots, L.q, L.k, L.v, L.o, L.log_gamma,
+                                      b->cu_seqlens, b->prefill_slots, b->n_prefill, b->H, b->D,
+                                      b->chunk_size, bf16, s);
+      if (e == hipSuccess && b->n_decode > 0)
+        e = hy::launch_linear_decode(base, p->n_slots, (const char*)L.q + off,
+                                     (const char*)L.k + off, (const char*)L.v + off,
+                                     (char*)L.o + off,
+                                     L.log_gamma ? L.log_gamma + (size_t)n_prefill_tok * b->H : nullptr,
+                                     b->decode_slots, b->n_decode, b->H, b->D, bf16, s);
     } else {
-      st = hyattn_paged_append(L.k, L.v, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
-                               b->max_blocks_per_seq, b->context_lens, b->cu_q_lens, B,
-                               b->n_prefill > 0 ? (b->max_prefill_len > 1 ? b->max_prefill_len : 1)
-                                                : 1,
-                               b->H_kv, b->D, b->dtype, stream);
-      if (st != HYATTN_OK) return st;
-      if (b->n_prefill > 0) {
-        st = hyattn_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
-                                  b->max_blocks_per_seq, b->context_lens, b->cu_seqlens,
-                                  b->max_prefill_len, b->n_prefill, b->H, b->H_kv, b->D, b->scale,
-                                  b->dtype, stream);
-        if (st != HYATTN_OK) return st;
-      }
-      if (b->n_decode > 0) {
-        const size_t off = (size_t)n_prefill_tok * row_h;
-        st = hyattn_paged_decode((const char*)L.q + off, (char*)L.o + off, L.k_pool, L.v_pool,
-                                 b->n_blocks, b->block_tables + (size_t)b->n_prefill * b->max_blocks_per_seq,
-                                 b->max_blocks_per_seq, b->context_lens + b->n_prefill,
-                                 b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
-                                 b->workspace, b->workspace_bytes, b->dtype, stream);
-        if (st != HYATTN_OK) return st;
-      }
+      e = hy::launch_paged_append(L.k, L.v, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
+                                  b->max_blocks_per_seq, b->context_lens, b->cu_q_lens, B,
+                                  max_q_len, b->H_kv, b->D, bf16, s);
+      if (e == hipSuccess && b->n_prefill > 0 && b->max_prefill_len > 0)
+        e = hy::launch_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
+                                     b->max_blocks_per_seq, b->context_lens, b->cu_seqlens,
+                                     b->max_prefill_len, b->n_prefill, b->H, b->H_kv, b->D,
+                                     b->scale, bf16, s);
+      if (e == hipSuccess && b->n_decode > 0)
+        e = hy::launch_paged_decode((const char*)L.q + off, (char*)L.o + off, L.k_pool, L.v_pool,
+                                    b->n_blocks,
+                                    b->block_tables + (size_t)b->n_prefill * b->max_blocks_per_seq,
+                                    b->max_blocks_per_seq, b->context_lens + b->n_prefill,
+                                    b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
+                                    b->workspace, bf16, s);
     }
+    if (e != hipSuccess) return hip_status(e, "hybrid step launch");
   }
   return ok();
 }
