@@ -207,6 +207,27 @@ hyattn_status hyattn_paged_decode(const void* q, void* o, const void* k_pool, co
                                   void* workspace, size_t workspace_bytes, hyattn_dtype dtype,
                                   void* stream);
 
+/* Decode attention exactly as hyattn_paged_decode (same arguments, same
+ * kernels, same results bit for bit), for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It takes no workspace: its partition partials and scan live
+ * in a file-scope device array of HYATTN_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends, whose address is looked up on the first call on each
+ * device. It calls no hipMalloc, hipFree or allocating routine. A bf16 call
+ * that needs more scratch than that (hyattn_paged_decode_workspace_bytes sizes
+ * the worst case; at most B * H_q * 64 * (D + 2) * 4 bytes plus the scan) fails
+ * with HYATTN_ERR_INVALID_ARG before launching. Every call on a GPU shares its
+ * array, so calls that overlap on one GPU (other streams, other threads) race;
+ * nothing in the array needs to start at zero (each call writes what it reads).
+ * fp32 I/O uses no scratch. */
+#define HYATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hyattn_status hyattn_paged_decode_noalloc(const void* q, void* o, const void* k_pool,
+                                          const void* v_pool, int64_t n_blocks,
+                                          const int32_t* block_tables_dev, int max_blocks_per_seq,
+                                          const int32_t* context_lens_dev, int max_context, int B,
+                                          int H_q, int H_kv, int D, float scale,
+                                          hyattn_dtype dtype, void* stream);
+
 /* Causal prefill attention over paged KV (FlashAttention-style, P2 §2.3): the
  * i-th query of request r (row cu_q_lens[r] + i of q/o, [N_q][H_q][D]) sits at
  * position context_lens[r] - q_len_r + i and attends to keys 0 .. that

@@ -43,6 +43,13 @@ struct DecodePlan {
 // sizes the workspace)
 DecodePlan decode_plan(int max_context, int64_t work_pairs);
 size_t decode_workspace_bytes(int B, int H_q, int D, int max_context);
+// bytes of workspace one launch_paged_decode call of these sizes uses
+size_t decode_launch_bytes(int B, int H_q, int H_kv, int D, int max_context);
+// Device address of this device's scratch array (kDecodeScratchBytes), looked
+// up on the first call on each device; the allocation-free decode uses it as
+// its workspace.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+hipError_t decode_scratch(void** out);
 
 hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
                                int64_t n_blocks, const int32_t* bt, int max_blocks,

@@ -19,6 +19,9 @@
 
 #include "hy_kernels.hpp"
 
+static_assert(HYATTN_NOALLOC_SCRATCH_BYTES == hy::kDecodeScratchBytes,
+              "the header states the scratch size of the allocation-free decode");
+
 struct hyattn_state_pool {
   float* base;
   size_t bytes;
@@ -431,11 +434,13 @@ size_t hyattn_paged_decode_workspace_bytes(int B, int H_q, int D, int max_contex
   return hy::decode_workspace_bytes(B, H_q, D, max_context);
 }
 
-hyattn_status hyattn_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
-                                  int64_t n_blocks, const int32_t* bt, int max_blocks,
-                                  const int32_t* ctx, int max_context, int B, int H_q, int H_kv,
-                                  int D, float scale, void* workspace, size_t workspace_bytes,
-                                  hyattn_dtype dtype, void* stream) {
+// Arguments of a decode call other than its workspace (and, in checked mode,
+// the tables and context lengths).
+static hyattn_status paged_decode_args(const void* q, const void* o, const void* k_pool,
+                                       const void* v_pool, int64_t n_blocks, const int32_t* bt,
+                                       int max_blocks, const int32_t* ctx, int max_context, int B,
+                                       int H_q, int H_kv, int D, hyattn_dtype dtype,
+                                       hipStream_t s) {
   hyattn_status st = check_full_dims(B, H_q, H_kv, D, dtype, n_blocks, max_blocks);
   if (st != HYATTN_OK) return st;
   if (max_context < 0 || (int64_t)max_context > (int64_t)max_blocks * 16)
@@ -448,16 +453,53 @@ hyattn_status hyattn_paged_decode(const void* q, void* o, const void* k_pool, co
   if (B == 0) return ok();
   if (!q || !o || !k_pool || !v_pool || !bt || !ctx)
     return fail(HYATTN_ERR_INVALID_ARG, "a pointer is NULL");
+  if (checked_mode() &&
+      (st = check_tables(bt, B, max_blocks, ctx, max_context, n_blocks, s)) != HYATTN_OK)
+    return st;
+  return ok();
+}
+
+hyattn_status hyattn_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
+                                  int64_t n_blocks, const int32_t* bt, int max_blocks,
+                                  const int32_t* ctx, int max_context, int B, int H_q, int H_kv,
+                                  int D, float scale, void* workspace, size_t workspace_bytes,
+                                  hyattn_dtype dtype, void* stream) {
+  hipStream_t s = as_stream(stream);
+  hyattn_status st = paged_decode_args(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx,
+                                       max_context, B, H_q, H_kv, D, dtype, s);
+  if (st != HYATTN_OK || B == 0) return st;
   const size_t need = hy::decode_workspace_bytes(B, H_q, D, max_context);
   if (dtype == HYATTN_BF16 && (!workspace || workspace_bytes < need))
     return fail(HYATTN_ERR_INVALID_ARG, "workspace needs %zu bytes (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
+  return hip_status(hy::launch_paged_decode(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx,
+                                            max_context, B, H_q, H_kv, D, scale, workspace,
+                                            dtype == HYATTN_BF16, s),
+                    "paged decode launch");
+}
+
+hyattn_status hyattn_paged_decode_noalloc(const void* q, void* o, const void* k_pool,
+                                          const void* v_pool, int64_t n_blocks, const int32_t* bt,
+                                          int max_blocks, const int32_t* ctx, int max_context,
+                                          int B, int H_q, int H_kv, int D, float scale,
+                                          hyattn_dtype dtype, void* stream) {
   hipStream_t s = as_stream(stream);
-  if (checked_mode() &&
-      (st = check_tables(bt, B, max_blocks, ctx, max_context, n_blocks, s)) != HYATTN_OK)
-    return st;
-  return hip_status(hy::launch_paged_decode(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx, max_context,
-                                            B, H_q, H_kv, D, scale, workspace,
+  hyattn_status st = paged_decode_args(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx,
+                                       max_context, B, H_q, H_kv, D, dtype, s);
+  if (st != HYATTN_OK || B == 0) return st;
+  void* ws = nullptr;
+  if (dtype == HYATTN_BF16) {
+    const size_t need = hy::decode_launch_bytes(B, H_q, H_kv, D, max_context);
+    if (need > hy::kDecodeScratchBytes)
+      return fail(HYATTN_ERR_INVALID_ARG,
+                  "decode of B=%d, H_q=%d, D=%d, max_context=%d needs %zu bytes of scratch; the "
+                  "allocation-free entry point holds %zu (use hyattn_paged_decode with a workspace)",
+                  B, H_q, D, max_context, need, hy::kDecodeScratchBytes);
+    hipError_t e = hy::decode_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "looking up the decode scratch array");
+  }
+  return hip_status(hy::launch_paged_decode(q, o, k_pool, v_pool, n_blocks, bt, max_blocks, ctx,
+                                            max_context, B, H_q, H_kv, D, scale, ws,
                                             dtype == HYATTN_BF16, s),
                     "paged decode launch");
 }

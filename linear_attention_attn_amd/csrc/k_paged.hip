@@ -14,6 +14,8 @@
 // scale * log2(e), with the running maximum subtracted (fp32 throughout).
 #include <math.h>
 
+#include <mutex>
+
 #include "hy_common.hpp"
 #include "hy_kernels.hpp"
 
@@ -116,6 +118,41 @@ static size_t decode_partials_bytes(int B, int H_q, int D, int max_parts) {
 size_t decode_workspace_bytes(int B, int H_q, int D, int max_context) {
   const DecodePlan p = decode_plan(max_context, 0);  // the most partitions any launch uses
   return decode_partials_bytes(B, H_q, D, p.max_parts) + ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+size_t decode_launch_bytes(int B, int H_q, int H_kv, int D, int max_context) {
+  const DecodePlan p = decode_plan(max_context, (int64_t)B * H_kv);  // as launch_paged_decode
+  return decode_partials_bytes(B, H_q, D, p.max_parts) + ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+// ============================================================================
+// Scratch of the allocation-free decode entry point: the partition partials
+// and the partition scan live in this file-scope device array instead of a
+// caller's workspace. Each GPU the library runs on holds its own copy until
+// the process ends. In host code the array's name is only a stand-in, so its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever handed to kernels.
+// ============================================================================
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 __device__ __forceinline__ int n_parts_of(int c, int max_blocks, int part_blocks, int max_parts) {

@@ -34,7 +34,7 @@ EXPORTS = (
     "hyattn_paged_prefill", "hyattn_hybrid_workspace_bytes", "hyattn_hybrid_step",
     "hyattn_estimate_memory",
     "hyattn_linear_prefill_chunked_gated", "hyattn_linear_decode_gated",
-    "hyattn_bucket_by_length",
+    "hyattn_bucket_by_length", "hyattn_paged_decode_noalloc",
 )
 
 
@@ -109,6 +109,8 @@ def load():
                                  vp], st),
         "hyattn_paged_prefill": ([vp, vp, vp, vp, i64, vp, i, vp, vp, i, i, i, i, i, f, i, vp],
                                  st),
+        "hyattn_paged_decode_noalloc": ([vp, vp, vp, vp, i64, vp, i, vp, i, i, i, i, i, f, i, vp],
+                                        st),
         "hyattn_hybrid_workspace_bytes": ([C.POINTER(Batch)], sz),
         "hyattn_hybrid_step": ([vp, i, C.POINTER(LayerIO), C.POINTER(Batch), vp, vp], st),
         "hyattn_estimate_memory": ([vp, i, i, i, i, vp, i, i, i, C.POINTER(MemoryEstimate)], st),
@@ -254,6 +256,15 @@ def hyattn_paged_decode(q, o, k_pool, v_pool, n_blocks, block_tables, max_blocks
                                       ptr(block_tables), max_blocks_per_seq, ptr(context_lens),
                                       max_context, B, H_q, H_kv, D, float(scale), ptr(workspace),
                                       workspace_bytes, dtype, _stream(stream)))
+
+
+def hyattn_paged_decode_noalloc(q, o, k_pool, v_pool, n_blocks, block_tables, max_blocks_per_seq,
+                                context_lens, max_context, B, H_q, H_kv, D, scale, dtype,
+                                stream=None):
+    _check(load().hyattn_paged_decode_noalloc(ptr(q), ptr(o), ptr(k_pool), ptr(v_pool), n_blocks,
+                                              ptr(block_tables), max_blocks_per_seq,
+                                              ptr(context_lens), max_context, B, H_q, H_kv, D,
+                                              float(scale), dtype, _stream(stream)))
 
 
 def hyattn_paged_prefill(q, o, k_pool, v_pool, n_blocks, block_tables, max_blocks_per_seq,
