@@ -55,6 +55,38 @@ def _prefill(hy, pool, layer, q, k, v, cu, slots, chunk, dtype):
 
 
 # ----------------------------------------------------------------- decode --
+@pytest.mark.parametrize("B,D", [(37, 128), (53, 64)])
+def test_decode_batch_with_several_states_per_workgroup(hy, B, D):
+    """A batch between one and the split threshold's worth of (request, head) units: the
+    persistent decode walks 2-3 states per workgroup, in an order unrelated to the slots
+    (slots reversed and gapped). Every unit against the oracle, two steps in a row, and
+    the slots outside the batch untouched."""
+    import torch
+    rng = np.random.default_rng(140 + B)
+    H = 32
+    pool = Pool(hy, 1, 2 * B + 1, H, D)
+    all_slots = pool.alloc(2 * B + 1)
+    slots = all_slots[::-2][:B]  # every other slot, descending
+    others = sorted(set(all_slots) - set(slots))
+    pool.view[...] = 5.0
+    S0 = (rng.standard_normal((B, H, D, D)) * 0.1).astype(np.float32)
+    for r, s in enumerate(slots):
+        pool.view[0, s] = torch.from_numpy(S0[r]).cuda()
+    st = S0.astype(np.float64)
+    for step in range(2):
+        q, k, v = (synth.normal(rng, (B, H, D), D ** -0.5, "bf16") for _ in range(3))
+        do = torch.full_like(gu.dev(q), float("nan"))
+        hy.hyattn_linear_decode(pool.handle, 0, gu.dev(q), gu.dev(k), gu.dev(v), do,
+                                gu.i32(slots), B, hy.BF16)
+        torch.cuda.synchronize()
+        want = ref.linear_decode(q, k, v, st)
+        gu.assert_bf16(gu.host(do), want, f"decode step {step}, B={B}")
+    got_S = np.stack([gu.host(pool.view[0, s]) for s in slots])
+    gu.assert_f32(got_S, st, "final states")
+    assert bool((pool.view[0, others] == 5.0).all()), "slots outside the batch changed"
+    pool.close()
+
+
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_decode_matches_oracle(hy, dtype, D):
     """Several decode steps from random prior states (mid-request decode)."""
