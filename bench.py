@@ -9,13 +9,19 @@ full layers with 8 KV heads in 16-token blocks. A step = zero the 16 prefill
 slots (request start) + hyattn_hybrid_step over all 32 layers. Throughput =
 tokens served per second (65 536 prefill + 240 decode tokens per step).
 
-Printed: one JSON line (see the keys below), with the roofline of the dominant
-kernel (paged decode, HBM-bound; HIP events around each of its launches) and
-the fp64 oracle's throughput on a bounded sample of the same workload.
+Printed: one JSON line (see the keys below), with
+  * the roofline of the dominant kernel (paged decode, HBM-bound; HIP events
+    around each of its launches),
+  * the step against the sum of its operations' roofline times (step_roofline),
+  * the first (cold) step beside the steady state (first_step_ms),
+  * each layer operation on a workload of its own (workloads: the 64-request
+    linear decode batch cold and back to back, the 8 x 8192-token chunked
+    prefill per chunk size with its first call, the B = 128 paged decode;
+    see kernel_workloads()), timed before the step's workload is allocated,
+  * per-operation times on the step's own data (components_ms_per_call),
+  * the fp64 oracle's throughput on a bounded sample of the same workload.
 
-`--kernel-workloads` instead times each layer operation on a workload of its own
-(linear decode batch, linear chunked prefill, paged decode) and prints one JSON
-line per workload; see kernel_workloads().
+`--kernel-workloads` prints only the per-operation workloads, one JSON line each.
 """
 from __future__ import annotations
 
@@ -188,12 +194,96 @@ class Workload:
         T, D = W["prefill_len"], self.D
         return self.n_p * self.H * 4 * D * (T * (T + 1) // 2)
 
+    def paged_append_bytes(self):
+        # each new token's K and V rows read once and written once into the pool
+        return self.N * self.Hkv * self.D * 2 * 2 * 2
+
+    def state_zero_bytes(self):
+        return self.n_lin * self.n_p * self.H * self.D * self.D * 4
+
+    def component_roofline_ms(self):
+        """Each operation of the step at its bound's peak (ms): HBM-bound ones on their
+        algorithmic bytes, the causal prefill on its algorithmic flops (MFMA-bound), the
+        linear prefill at the larger of its byte and flop times (bytes bind)."""
+        hbm = lambda b: b / (HBM_PEAK_GBS * 1e9) * 1e3
+        mfma = lambda f: f / (BF16_PEAK_TFLOPS * 1e12) * 1e3
+        return {"state_zero": hbm(self.state_zero_bytes()),
+                "linear_prefill": max(hbm(self.linear_prefill_bytes()), mfma(self.linear_prefill_flops())),
+                "linear_decode": hbm(self.linear_decode_bytes()),
+                "paged_append": hbm(self.paged_append_bytes()),
+                "paged_prefill": max(mfma(self.paged_prefill_flops()), hbm(self.N * self.H * self.D * 2 * 2)),
+                "paged_decode": hbm(self.decode_kv_bytes())}
+
 
 # ------------------------------------------------------------- components --
-def component_times(wl, reps=3, inner=5):
-    """Per-call device time of each layer operation, HIP events on torch's stream: the
-    median over `reps` event pairs, each around `inner` back-to-back calls (so the host's
-    launch latency of the first call does not count against a sub-millisecond kernel)."""
+def step_component_times(wl, steps=2):
+    """Per-call time of each operation inside the step. The step is issued decomposed:
+    the same launches as hyattn_hybrid_step, in the same order on the same data, through
+    the single-operation entry points, with a HIP event after each call on torch's stream.
+    Each interval is one operation with the step's own neighbours before and after it
+    (cache contents, clocks); means over its layers and `steps` steps. The sum of the
+    intervals is a whole step (reported as step_ms_decomposed)."""
+    import torch
+    hy = wl.hy
+    st = torch.cuda.current_stream()
+    n_p, n_d, P = wl.n_p, wl.n_d, W["prefill_len"]
+    off = n_p * P
+    lin, full = wl.lin, wl.full
+    row = lambda t: t[off:]
+    marks = []
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        marks.append((name, e))
+
+    wl.step()  # warm
+    torch.cuda.synchronize()
+    mark("start")
+    for _ in range(steps):
+        hy.hyattn_state_pool_zero(wl.pool, wl.slots_p, n_p)
+        mark("state_zero")
+        li = fi = 0
+        for t in wl.types:
+            if t == 0:
+                hy.hyattn_linear_prefill_chunked(wl.pool, li, lin["q"], lin["k"], lin["v"], lin["o"],
+                                                 wl.cu_p, wl.slots_p, n_p, W["chunk"], hy.BF16)
+                mark("linear_prefill")
+                hy.hyattn_linear_decode(wl.pool, li, row(lin["q"]), row(lin["k"]), row(lin["v"]),
+                                        row(lin["o"]), wl.slots_d, n_d, hy.BF16)
+                mark("linear_decode")
+                li += 1
+            else:
+                kp, vp = wl.pools[fi]
+                hy.hyattn_paged_append(full["k"], full["v"], kp, vp, wl.lay.n_blocks, wl.bt,
+                                       wl.lay.max_blocks, wl.ctx_d, wl.cu_q, n_p + n_d, P, wl.Hkv,
+                                       wl.D, hy.BF16)
+                mark("paged_append")
+                hy.hyattn_paged_prefill(full["q"], full["o"], kp, vp, wl.lay.n_blocks, wl.bt,
+                                        wl.lay.max_blocks, wl.ctx_d, wl.cu_p, P, n_p, wl.H, wl.Hkv,
+                                        wl.D, wl.D ** -0.5, hy.BF16)
+                mark("paged_prefill")
+                hy.hyattn_paged_decode(row(full["q"]), row(full["o"]), kp, vp, wl.lay.n_blocks,
+                                       wl.bt[n_p:], wl.lay.max_blocks, wl.ctx_d[n_p:], wl.max_context,
+                                       n_d, wl.H, wl.Hkv, wl.D, wl.D ** -0.5, wl.ws, wl.ws_bytes,
+                                       hy.BF16)
+                mark("paged_decode")
+                fi += 1
+    torch.cuda.synchronize()
+    acc = {}
+    for (_, e0), (name, e1) in zip(marks[:-1], marks[1:]):
+        acc.setdefault(name, []).append(e0.elapsed_time(e1))
+    out = {k: float(np.mean(v)) for k, v in acc.items()}
+    out["step_ms_decomposed"] = marks[0][1].elapsed_time(marks[-1][1]) / steps
+    return out
+
+
+def component_times(wl, reps=3, inner=5, names=None):
+    """Per-call device time of layer operations on their own, HIP events on torch's stream:
+    the median over `reps` event pairs, each around `inner` back-to-back calls of one
+    operation on the step's data. Used for the gated variants, which the step does not run;
+    the step's own operations are timed in place by step_component_times. `names` selects
+    operations (all by default)."""
     import torch
     hy = wl.hy
     st = torch.cuda.current_stream()
@@ -229,6 +319,8 @@ def component_times(wl, reps=3, inner=5):
     }
     out = {}
     for name, fn in calls.items():
+        if names is not None and name not in names:
+            continue
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -299,9 +391,8 @@ def copy_probe(reps=3):
                       "reps": reps}), flush=True)
 
 
-def kernel_workloads():
-    """Each layer operation on a workload of its own, HIP events on torch's stream, one
-    JSON line per workload (not the bench line):
+def kernel_workloads(emit=None):
+    """Each layer operation on a workload of its own, HIP events on torch's stream:
       * linear decode: B = 64, H = 32, D = 128, 256 steps from prior states ~ N(0, 0.1);
         cold steps (a 1 GiB write between steps, untimed, evicts the 134 MB of state from
         L2 and the MALL) and the mean over 256 back-to-back steps;
@@ -310,14 +401,17 @@ def kernel_workloads():
         call, then the median of 10 after 3 warm-ups;
       * paged decode: B = 128, H_q = 32, H_kv = 8, D = 128, contexts uniform in
         [512, 32768], 16-token blocks in a permuted pool with 1024 NaN spare blocks:
-        median of 20 after 5 warm-ups.
+        the first call, then the median of 20 after 5 warm-ups.
     A GPU-side sleep ahead of each timed call lets the host enqueue the events and the
-    launch before the GPU reaches them, so host launch latency is not timed."""
+    launch before the GPU reaches them, so host launch latency is not timed. Returns a
+    dict of the three workloads' figures (emit: called with each one as it is done).
+    Every device buffer is released before returning."""
     import torch
     from linear_attention_attn_amd import hyattn as hy
     hy.load()
     st = torch.cuda.current_stream()
     dev = "cuda"
+    res = {}
 
     def timed(fn, before=None):
         if before is not None:
@@ -330,8 +424,10 @@ def kernel_workloads():
         e1.synchronize()
         return e0.elapsed_time(e1)
 
-    def emit(d):
-        print(json.dumps(d), flush=True)
+    def done(name, d):
+        res[name] = d
+        if emit is not None:
+            emit(dict({"kernel_workload": name}, **d))
 
     # ---- linear decode ----
     cfg = synth.WORKLOADS["linear_decode"]
@@ -349,8 +445,7 @@ def kernel_workloads():
     step_bytes = B * H * (2 * D * D * 4 + 4 * D * 2)
     call = lambda t: hy.hyattn_linear_decode(pool, 0, qkv[t, 0], qkv[t, 1], qkv[t, 2], out[t],
                                              sl, B, hy.BF16)
-    call(0)
-    torch.cuda.synchronize()
+    first = timed(lambda: call(0), before=lambda: scrub.fill_(-1.0))
     cold = [timed(lambda t=t: call(t), before=lambda t=t: scrub.fill_(float(t)))
             for t in range(steps)]
     torch.cuda._sleep(200_000)
@@ -362,13 +457,16 @@ def kernel_workloads():
     e1.synchronize()
     warm = e0.elapsed_time(e1) / steps
     tc = float(np.median(cold))
-    emit({"kernel_workload": "linear_decode", "shape": f"B={B} H={H} D={D} bf16 io, fp32 state",
-          "steps": steps, "bytes_per_step": step_bytes,
-          "cold_ms_median": round(tc, 5), "cold_tokens_per_s": round(B * steps / (sum(cold) * 1e-3), 1),
-          "cold_gbs": round(step_bytes / (tc * 1e-3) / 1e9, 1),
-          "cold_hbm_frac": round(step_bytes / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-          "back_to_back_ms": round(warm, 5),
-          "back_to_back_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1)})
+    done("linear_decode", {
+        "shape": f"B={B} H={H} D={D} bf16 io, fp32 state", "steps": steps,
+        "bytes_per_step": step_bytes, "first_call_ms": round(first, 5),
+        "cold_ms_median": round(tc, 5),
+        "cold_tokens_per_s": round(B * steps / (sum(cold) * 1e-3), 1),
+        "cold_gbs": round(step_bytes / (tc * 1e-3) / 1e9, 1),
+        "cold_hbm_frac": round(step_bytes / (tc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "back_to_back_ms": round(warm, 5),
+        "back_to_back_gbs": round(step_bytes / (warm * 1e-3) / 1e9, 1),
+        "back_to_back_hbm_frac": round(step_bytes / (warm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     hy.hyattn_state_pool_destroy(pool)
     del buf, qkv, out, scrub
 
@@ -398,6 +496,7 @@ def kernel_workloads():
     for _ in range(10):
         for C, fn in calls.items():
             reps[C].append(timed(fn, before=zero))
+    per_c = {}
     for C in cfg["chunks"]:
         t = float(np.median(reps[C]))
         # the chunk-size count of the method (Q.S, S update, causal pairs inside each
@@ -405,14 +504,15 @@ def kernel_workloads():
         flops_c = N * H * (4 * D * D + 2 * (C + 1) * D)
         flops_k = N * H * (4 * D * D + 2 * 33 * D)
         t_roof = max(pf_bytes / (HBM_PEAK_GBS * 1e9), flops_k / (BF16_PEAK_TFLOPS * 1e12))
-        emit({"kernel_workload": "linear_prefill", "shape": f"{B}x{T} tokens H={H} D={D} bf16 io",
-              "chunk": C, "first_call_ms": round(first[C], 4), "ms_median": round(t, 4),
-              "tokens_per_s": round(N / (t * 1e-3), 1), "bytes": pf_bytes,
-              "hbm_frac": round(pf_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-              "flops_chunk_count": flops_c,
-              "mfma_frac_chunk_count": round(flops_c / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-              "flops_kernel_count": flops_k,
-              "attainable_roof_frac": round(t_roof / (t * 1e-3), 4)})
+        per_c[str(C)] = {
+            "first_call_ms": round(first[C], 4), "ms_median": round(t, 4),
+            "tokens_per_s": round(N / (t * 1e-3), 1),
+            "hbm_frac": round(pf_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac_chunk_count": round(flops_c / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "attainable_roof_frac": round(t_roof / (t * 1e-3), 4)}
+    done("linear_prefill", {"shape": f"{B}x{T} tokens H={H} D={D} bf16 io", "bytes": pf_bytes,
+                            "flops_kernel_count": N * H * (4 * D * D + 2 * 33 * D),
+                            "chunks": per_c})
     hy.hyattn_state_pool_destroy(pool)
     del buf, q, k, v, o
 
@@ -436,15 +536,22 @@ def kernel_workloads():
     ctx_d = torch.as_tensor(ctx).to(dev)
     call = lambda: hy.hyattn_paged_decode(q, o, kp, vp, lay.n_blocks, bt, lay.max_blocks, ctx_d,
                                           maxc, B, Hq, Hkv, D, D ** -0.5, ws, wsb, hy.BF16)
+    first = timed(call)
     for _ in range(5):
         timed(call)
     t = float(np.median([timed(call) for _ in range(20)]))
     kv_bytes = int(ctx.astype(np.int64).sum()) * Hkv * D * 2 * 2
-    emit({"kernel_workload": "paged_decode", "shape": f"B={B} H_q={Hq} H_kv={Hkv} D={D} bf16 KV, "
-          f"contexts uniform in [{cfg['ctx_lo']}, {cfg['ctx_hi']}]",
-          "ms_median": round(t, 4), "tokens_per_s": round(B / (t * 1e-3), 1),
-          "kv_bytes": kv_bytes, "gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
-          "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    done("paged_decode", {
+        "shape": f"B={B} H_q={Hq} H_kv={Hkv} D={D} bf16 KV, contexts uniform in "
+                 f"[{cfg['ctx_lo']}, {cfg['ctx_hi']}]",
+        "first_call_ms": round(first, 4), "ms_median": round(t, 4),
+        "tokens_per_s": round(B / (t * 1e-3), 1), "kv_bytes": kv_bytes,
+        "gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
+        "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    del kp, vp, q, o, ws, bt, ctx_d, spare
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def dominant_kernel_roofline(wl, steps):
@@ -591,6 +698,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--no-kernel-workloads", action="store_true",
+                    help="skip the per-operation workloads (linear decode batch, 8x8192 "
+                         "chunked prefill, B=128 paged decode) in the bench line")
     ap.add_argument("--ctx-scale", type=float, default=1.0,
                     help="scale of the longest decode context (1.0 = 131072)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -608,15 +718,29 @@ def main():
         copy_probe()
         return
     if args.kernel_workloads:
-        kernel_workloads()
+        kernel_workloads(emit=lambda d: print(json.dumps(d), flush=True))
         return
     from linear_attention_attn_amd import hyattn as hy
     hy.load()
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} {props.gcnArchName} CUs={props.multi_processor_count} "
         f"mem={props.total_memory / 2**30:.0f} GiB")
+    workloads = None
+    if not args.no_kernel_workloads:
+        t0 = time.time()
+        workloads = kernel_workloads()
+        log(f"per-operation workloads took {time.time() - t0:.1f}s")
     wl = Workload(args.ctx_scale)
     st = torch.cuda.current_stream()
+    # the first step after the workload is set up, timed on its own (one-time costs
+    # such as loading the kernels' code and first-touch of the pools included)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    wl.step()
+    e1.record(st)
+    e1.synchronize()
+    first_ms = e0.elapsed_time(e1)
+    log(f"first step {first_ms:.3f} ms")
     for i in range(args.warmup):
         wl.step()
         torch.cuda.synchronize()
@@ -653,6 +777,18 @@ def main():
                    "layers": len(wl.types), "chunk": W["chunk"], "seq_len": W["prefill_len"],
                    "max_context": wl.max_context, "parallelism": "none (1 GPU)"},
     }
+    out["first_step_ms"] = round(first_ms, 4)
+    roof_ms = wl.component_roofline_ms()
+    sum_roof = (roof_ms["state_zero"] + wl.n_lin * (roof_ms["linear_prefill"] + roof_ms["linear_decode"])
+                + wl.n_full * (roof_ms["paged_append"] + roof_ms["paged_prefill"] + roof_ms["paged_decode"]))
+    out["step_roofline"] = {
+        "sum_component_roof_ms": round(sum_roof, 4), "frac": round(sum_roof / ms, 4),
+        "component_roof_ms": {k: round(v, 5) for k, v in roof_ms.items()},
+        "note": "each operation at its bound's peak (HBM 8 TB/s on its algorithmic bytes, or bf16 "
+                "MFMA 2.5 PFLOP/s on its algorithmic flops, whichever is longer), summed over the "
+                f"step's {wl.n_lin} linear and {wl.n_full} full layers; frac = that sum / ms_per_step"}
+    if workloads is not None:
+        out["workloads"] = workloads
     roof = dominant_kernel_roofline(wl, max(1, min(args.steps, 3)))
     log(f"dominant kernel: {roof}")
     out["device"] = {"name": props.gcnArchName, "peaks_used": {"hbm_gbs": HBM_PEAK_GBS,
@@ -663,25 +799,30 @@ def main():
     out["roofline"]["algorithmic_bytes_per_launch"] = roof["algorithmic_bytes_per_launch"]
     out["roofline"]["avg_launch_ms"] = roof["avg_launch_ms"]
     if not args.no_components:
-        comp = component_times(wl)
+        comp = step_component_times(wl)
+        alone = component_times(wl, names=("linear_prefill_gated", "linear_decode_gated"))
         n_lin, n_full = wl.n_lin, wl.n_full
         lp, ld, pd = comp["linear_prefill"], comp["linear_decode"], comp["paged_decode"]
         out["components_ms_per_call"] = {k: round(v, 4) for k, v in comp.items()}
+        out["components_gated_ms_per_call"] = {k: round(v, 4) for k, v in alone.items()}
         out["components"] = {
             "linear_decode_hbm_frac": round(wl.linear_decode_bytes() / (ld * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "paged_decode_hbm_frac": round(wl.decode_kv_bytes() / (pd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "linear_prefill_mfma_frac": round(wl.linear_prefill_flops() / (lp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "linear_prefill_hbm_frac": round(wl.linear_prefill_bytes() / (lp * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "linear_prefill_gated_mfma_frac": round(
-                wl.linear_prefill_flops(gated=True) / (comp["linear_prefill_gated"] * 1e-3) / 1e12
+                wl.linear_prefill_flops(gated=True) / (alone["linear_prefill_gated"] * 1e-3) / 1e12
                 / BF16_PEAK_TFLOPS, 4),
             "linear_decode_gated_hbm_frac": round(
-                wl.linear_decode_bytes(gated=True) / (comp["linear_decode_gated"] * 1e-3) / 1e9
+                wl.linear_decode_bytes(gated=True) / (alone["linear_decode_gated"] * 1e-3) / 1e9
                 / HBM_PEAK_GBS, 4),
             "paged_prefill_mfma_frac": round(wl.paged_prefill_flops() / (comp["paged_prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "step_ms_from_components": round(comp["state_zero"] + n_lin * (lp + ld) + n_full * (
                 comp["paged_append"] + comp["paged_prefill"] + pd), 3),
         }
+        roof_ms = out["step_roofline"]["component_roof_ms"]
+        out["step_roofline"]["component_frac"] = {
+            k: round(roof_ms[k] / comp[k], 4) for k in roof_ms if k in comp}
     if not args.no_cpu_baseline:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -9,6 +9,10 @@
 //   §2.4  chunked prefill carries S from chunk to chunk.
 // Layout: states fp32 [layer][slot][H][D][D] with S[i][j] at i * D + j
 // (row i = key dim, column j = value dim); q/k/v/o token-major [N][H][D].
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "hy_common.hpp"
 #include "hy_kernels.hpp"
 
@@ -853,11 +857,25 @@ size_t linear_prefill_bf16_lds_bytes(int D, int C, bool gated) {
   return D == 128 ? prefill_bf16_lds_bytes<128>(C, gated) : prefill_bf16_lds_bytes<64>(C, gated);
 }
 
+// Dynamic LDS above 64 KiB must be allowed per device function and device.
+// The allowance is raised only when a launch needs more than it already
+// grants: hipFuncSetAttribute on every launch costs host time that would
+// show between short back-to-back launches.
 template <typename K>
 static hipError_t allow_lds(K kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> allowed;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_pair(reinterpret_cast<const void*>(kernel), dev);
+  std::lock_guard<std::mutex> lk(mu);
+  size_t& have = allowed[key];
+  if (have >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(key.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q, const void* k,
