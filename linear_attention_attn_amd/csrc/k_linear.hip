@@ -853,6 +853,288 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
         S[(int64_t)state_row(t, 4 * lg + i) * D + dv0 + 16 * n + lr] = Sacc[t][n][i];
 }
 
+// ============================================================================
+// Chunked prefill, bf16 I/O, D = 128, on v_mfma_f32_32x32x16_bf16.
+//
+// The same streaming form as k_linear_prefill_bf16 (same LDS ring of 32-token
+// K, V and Q tiles, same loads, same per-block arithmetic), with every product
+// on 32x32 tiles: wave w owns the 32 value columns v0 = 32 w .. v0 + 31 of the
+// fp32 state, held as four 32x32 accumulator tiles (key dims 32 t .. 32 t + 31).
+// Per block, per wave:
+//   O^T = S^T Q^T             8 k steps of 16 key dims, S split hi + lo
+//   P^T = K Q^T               the same 8 k steps (each Q fragment serves both)
+//   O^T += V^T tril(P)^T      2 k steps of 16 keys, P split hi + lo
+//   S  += K^T V               4 tiles x 2 k steps of 16 tokens
+// Rows of every 32-row operand are permuted by perm32 (see below), so that the
+// accumulator elements a lane holds are, per half-tile, eight consecutive
+// indices: exactly the k operand the next product needs, with no data
+// movement between lanes; the output then leaves as 16-byte pieces. The
+// contractions' operands otherwise come straight from the row-major tiles
+// (16-byte reads) or through transposing reads (K^T, V^T).
+// ============================================================================
+
+// Tile row m = 8 g + 4 h + j (g = 0..3, h = 0..1, j = 0..3) of a 32-row MFMA
+// operand stands for index perm32(m) = 16 (g >> 1) + 8 h + 4 (g & 1) + j of the
+// 32 key dims, keys or value columns it covers. A lane of half h (lanes 32 h ..
+// 32 h + 31) then receives in accumulator element i the index
+// 16 (i >> 3) + 8 h + (i & 7).
+__device__ __forceinline__ int perm32(int m) {
+  const int g = m >> 3;
+  return 16 * (g >> 1) + 8 * ((m >> 2) & 1) + 4 * (g & 1) + (m & 3);
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(256, 2) void k_linear_prefill_m32(
+    float* __restrict__ states, int n_slots, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+    const float* __restrict__ log_gamma, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ slots, int H) {
+  constexpr int D = 128;
+  using R = LinRing<D, GATED>;
+  constexpr int CPR = R::CPR, RPI = R::RPI;
+  constexpr int TILE = R::TILE, IPT = R::IPT, IPB = R::IPB, VMB = R::VMB;
+  extern __shared__ __align__(16) uint16_t lds_h[];
+
+  const int unit = blockIdx.x;
+  const int r = unit / H, h = unit - (unit / H) * H;
+  const int tok0 = cu[r], T = cu[r + 1] - tok0;
+  const int slot = slots[r];
+  if (T <= 0 || slot < 0 || slot >= n_slots) return;
+  const int nb = (T + kLinBlock - 1) / kLinBlock;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int lc = l & 31, hl = l >> 5;        // MFMA column of the lane, its half
+  const int gi = l & 15, gq = (l >> 4) & 1;  // place in its 16-lane group, the group's half-tile
+  const int v0 = 32 * w;
+  float* S = states + ((int64_t)slot * H + h) * (int64_t)(D * D);
+  const int64_t ldx = (int64_t)H * D;
+  const uint16_t* qb = q + (int64_t)tok0 * ldx + (int64_t)h * D;
+  const uint16_t* kb = k + (int64_t)tok0 * ldx + (int64_t)h * D;
+  const uint16_t* vb = v + (int64_t)tok0 * ldx + (int64_t)h * D;
+  uint16_t* ob = o + (int64_t)tok0 * ldx + (int64_t)h * D;
+
+  // ---- block loads (as k_linear_prefill_bf16) ----
+  static_assert(IPT % 4 == 0, "pieces of a tensor split evenly over 4 waves");
+  auto piece_row = [&](int i) { return ((4 * i) % IPT + w) * RPI + l / CPR; };
+  auto piece_swz = [&](int i, int row) {
+    const int tensor = 4 * i / IPT;
+    return tensor == 0 ? kswz<D>(row) : (tensor == 1 ? vswz<D>(row) : qswz<D>(row));
+  };
+  auto issue = [&](int b, int sl) {
+    uint16_t* base = lds_h + sl * R::SLOT;
+    const int64_t blk = (int64_t)(kLinBlock * b) * ldx;
+    const int last = T - 1 - kLinBlock * b;  // last valid row of the block
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int tensor = 4 * i / IPT;
+      const int row = piece_row(i);
+      const int rr = min(row, last);
+      const uint32_t off = (uint32_t)__mul24(rr, (int)ldx) + 8 * ((l % CPR) ^ piece_swz(i, row));
+      const uint16_t* src = (tensor == 0 ? kb : (tensor == 1 ? vb : qb)) + blk + off;
+      uint16_t* dst = base + tensor * TILE + ((4 * i) % IPT + w) * RPI * D;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    if constexpr (GATED) {  // this wave's copy of the block's forget factors (lanes 32..63 repeat)
+      const int tok = min(kLinBlock * b + (l & 31), T - 1);
+      const float* src = log_gamma + (int64_t)(tok0 + tok) * H + h;
+      uint16_t* dst = base + 3 * TILE + w * 128;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+  };
+  auto clear_tail = [&](int sl, int n) {  // V rows past the request's end become zeros
+    uint16_t* base = lds_h + sl * R::SLOT;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int row = piece_row(i);
+      if (4 * i / IPT == 1 && row >= n)
+        *reinterpret_cast<u32x4*>(base + TILE + ((4 * i) % IPT + w) * RPI * D + 8 * l) =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // ---- transposing reads: eight consecutive rows 16 c + 8 hl + 0..7 of one
+  // column of a tile, the column being base + perm32(lc). The lane's source
+  // address is row 16 c + 8 hl + gi / 4 (and 4 rows on), 4-column piece
+  // base + 16 gq + {0, 8, 4, 12}[gi % 4]: within each 16-lane group this hands
+  // lane gi the column perm32(16 gq + gi).
+  auto tr8 = [&](const uint16_t* tile, int c, int base, bool is_k) -> u32x4 {
+    const int row = 16 * c + 8 * hl + (gi >> 2);
+    const int col = base + 16 * gq + 8 * (gi & 1) + 4 * ((gi >> 1) & 1);
+    const uint16_t* p = tile + swz_off<D>(row, col, is_k ? kswz<D>(row) : vswz<D>(row));
+    const u32x2 a = ds_read_tr16_raw(p);
+    const u32x2 b2 = ds_read_tr16_raw(p + 4 * D);
+    return u32x4{a[0], a[1], b2[0], b2[1]};
+  };
+
+  // state tiles: Sacc[t][i] = S[32 t + 16 (i >> 3) + 8 hl + (i & 7)][v0 + perm32(lc)]
+  f32x16 Sacc[4];
+  const int vcol = v0 + perm32(lc);
+  {
+    const float* Sin = S + (int64_t)(8 * hl) * D + vcol;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Sacc[t][i] = Sin[(32 * t + 16 * (i >> 3) + (i & 7)) * D];
+  }
+
+#pragma unroll
+  for (int i = 0; i < kLinRing - 1; ++i)
+    if (i < nb) issue(i, i);
+
+  for (int b = 0; b < nb; ++b) {
+    const int sl = b % kLinRing;
+    const int n = min(kLinBlock, T - kLinBlock * b);
+    if (b + 1 < nb) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VMB));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    if (n < kLinBlock) clear_tail(sl, n);
+    lds_barrier();  // block b visible to all waves; block b - 1's slot is free
+    if (b + kLinRing - 1 < nb) issue(b + kLinRing - 1, (b + kLinRing - 1) % kLinRing);
+
+    const uint16_t* Kt = lds_h + sl * R::SLOT;
+    const uint16_t* Vt = Kt + TILE;
+    const uint16_t* Qt = Vt + TILE;
+
+    // gated: L of the lane's query row lc and of its keys 16 a + 8 hl + e
+    float lrow = 0.f, lkey[2][8], last = 0.f;
+    if constexpr (GATED) {
+      const float* gw = reinterpret_cast<const float*>(Qt + TILE) + w * 64;
+      float x = ((l & 31) < n) ? gw[l & 31] * kLog2e : 0.f;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(x, off, 32);
+        if ((l & 31) >= off) x += y;
+      }
+      lrow = __shfl(x, lc, 64);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lkey[a][e] = __shfl(x, 16 * a + 8 * hl + e, 64);
+      last = __shfl(x, 31, 64);
+    }
+
+    // O^T = S^T Q^T and P^T = K Q^T, one 16-wide k step s at a time: the Q
+    // fragment (query row lc, dims 16 s + 8 hl .. + 7) serves both; the
+    // fragments of step s + 1 are requested before the products of step s
+    f32x16 Ot, Pt;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      Ot[i] = 0.f;
+      Pt[i] = 0.f;
+    }
+    const int krow = perm32(lc);
+    auto load_qk = [&](int s, u32x4& qf, u32x4& kf) {
+      qf = *reinterpret_cast<const u32x4*>(Qt + swz_off<D>(lc, 16 * s + 8 * hl, qswz<D>(lc)));
+      kf = *reinterpret_cast<const u32x4*>(Kt + swz_off<D>(krow, 16 * s + 8 * hl, kswz<D>(krow)));
+    };
+    u32x4 qf, kf;
+    load_qk(0, qf, kf);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 qn, kn;
+      if (s + 1 < 8) load_qk(s + 1, qn, kn);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = Sacc[s >> 1][8 * (s & 1) + e];
+      u32x4 shi, slo;
+      split8(x, shi, slo);
+      Ot = mfma32x32x16(shi, qf, Ot);
+      Ot = mfma32x32x16(slo, qf, Ot);
+      Pt = mfma32x32x16(kf, qf, Pt);
+      if (s + 1 < 8) {
+        qf = qn;
+        kf = kn;
+      }
+      // keep the scheduler from hoisting later steps' reads and splits (they
+      // would hold many more registers than one step ahead needs)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (GATED) Ot *= fast_exp2(lrow);
+
+    // causal scores of query row lc: element i is key 16 (i >> 3) + 8 hl + (i & 7)
+    u32x4 phi[2], plo[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = 16 * a + 8 * hl + e;
+        float p = Pt[8 * a + e];
+        if constexpr (GATED) p *= fast_exp2(lrow - lkey[a][e]);
+        pv[e] = (key <= lc) ? p : 0.f;
+      }
+      split8(pv, phi[a], plo[a]);
+    }
+
+    // O^T += V^T P^T: V^T rows = value columns v0 + perm32(lc), keys 16 c + 8 hl + e
+    u32x4 vt[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) vt[c] = tr8(Vt, c, v0, false);
+    lds_wait_all(vt);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      Ot = mfma32x32x16(vt[c], phi[c], Ot);
+      Ot = mfma32x32x16(vt[c], plo[c], Ot);
+    }
+
+    // element i of Ot: value column v0 + 16 (i >> 3) + 8 hl + (i & 7) of query row lc
+    if (lc < n) {
+      uint16_t* orow = ob + (int64_t)(kLinBlock * b) * ldx + (uint32_t)(lc * (int)ldx + v0 + 8 * hl);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        u32x4 piece;
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) piece[p2] = pack_bf16x2(Ot[8 * a + 2 * p2], Ot[8 * a + 2 * p2 + 1]);
+        *reinterpret_cast<u32x4*>(orow + 16 * a) = piece;
+      }
+    }
+
+    // S += K^T V (gated: S = exp(L_last) S + K^T diag(exp(L_last - L_c)) V)
+    u32x4 vw_hi[2], vw_lo[2];
+    if constexpr (GATED) {
+      const float decay = fast_exp2(last);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Sacc[t] *= decay;
+      // vt[c] holds V of tokens 16 c + 8 hl + e
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          x[2 * p2] = bf16_lo(vt[c][p2]) * fast_exp2(last - lkey[c][2 * p2]);
+          x[2 * p2 + 1] = bf16_hi(vt[c][p2]) * fast_exp2(last - lkey[c][2 * p2 + 1]);
+        }
+        split8(x, vw_hi[c], vw_lo[c]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 kt[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) kt[c] = tr8(Kt, c, 32 * t, true);
+      lds_wait_all(kt);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (GATED) {
+          Sacc[t] = mfma32x32x16(kt[c], vw_hi[c], Sacc[t]);
+          Sacc[t] = mfma32x32x16(kt[c], vw_lo[c], Sacc[t]);
+        } else {
+          Sacc[t] = mfma32x32x16(kt[c], vt[c], Sacc[t]);
+        }
+      }
+    }
+  }
+
+  // the state's addresses again (an opaque copy of the column keeps the
+  // compiler from holding the load's 64 addresses across the whole loop)
+  int vcol_out = vcol, hl_out = hl;
+  asm volatile("" : "+v"(vcol_out), "+v"(hl_out));
+  float* Sout = S + (int64_t)(8 * hl_out) * D + vcol_out;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Sout[(32 * t + 16 * (i >> 3) + (i & 7)) * D] = Sacc[t][i];
+}
+
 size_t linear_prefill_bf16_lds_bytes(int D, int C, bool gated) {
   return D == 128 ? prefill_bf16_lds_bytes<128>(C, gated) : prefill_bf16_lds_bytes<64>(C, gated);
 }
@@ -878,6 +1160,25 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
   return e;
 }
 
+// Compute units of the current device (cached per device).
+static hipError_t device_cus(int* out) {
+  static std::mutex mu;
+  static std::map<int, int> cus;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cus.find(dev);
+  if (it == cus.end()) {
+    int n = 0;
+    if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return e;
+    it = cus.emplace(dev, n).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q, const void* k,
                                  const void* v, void* o, const float* log_gamma,
                                  const int32_t* cu, const int32_t* slots, int n_req, int H, int D,
@@ -897,7 +1198,23 @@ hipError_t launch_linear_prefill(float* layer_states, int n_slots, const void* q
                        n_slots, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,    \
                        (uint16_t*)o, log_gamma, cu, slots, H, chunk);                          \
   } while (0)
-    if (D == 128) {
+    int cus = 0;
+    if ((e = device_cus(&cus)) != hipSuccess) return e;
+    // One workgroup per CU: the 32x32-tile kernel (half the matrix instructions
+    // lets one wave per SIMD keep pace with the loads). Two or more per CU: the
+    // 16x16-tile kernel, whose co-resident waves overlap their phases as well.
+    if (D == 128 && (int64_t)n_req * H <= cus) {
+      const size_t lds = prefill_bf16_lds_bytes<128>(chunk, gated);
+#define HY_LP32(GG)                                                                            \
+  do {                                                                                         \
+    if ((e = allow_lds(k_linear_prefill_m32<GG>, lds)) != hipSuccess) return e;                \
+    hipLaunchKernelGGL((k_linear_prefill_m32<GG>), grid, block, lds, s, layer_states, n_slots, \
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,             \
+                       (uint16_t*)o, log_gamma, cu, slots, H);                                 \
+  } while (0)
+      if (gated) HY_LP32(true); else HY_LP32(false);
+#undef HY_LP32
+    } else if (D == 128) {
       if (gated) HY_LP(128, true); else HY_LP(128, false);
     } else {
       if (gated) HY_LP(64, true); else HY_LP(64, false);

@@ -166,6 +166,46 @@ def test_prefill_matches_oracle(hy, dtype, D, chunk):
     pool.close()
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_prefill_with_more_units_than_compute_units(hy, gated):
+    """bf16, D = 128, with more (request, head) units than the device has compute
+    units, so that workgroups share CUs and the launcher takes the 16x16-tile
+    kernel (the other tests' batches give each unit a CU of its own and run the
+    32x32-tile kernel): ragged requests, empty and single-token ones included,
+    from non-zero prior states."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(450 + gated)
+    H, D = 8, 128
+    B = cus // H + 9
+    lens = [(1, 77, 0, 33, 64, 5, 31, 32)[r % 8] for r in range(B)]
+    assert B * H > cus
+    cu = synth.cu_lens(lens)
+    N = int(cu[-1])
+    q, k, v = (synth.normal(rng, (N, H, D), D ** -0.5, "bf16") for _ in range(3))
+    g = synth.log_forget(rng, (N, H)) if gated else None
+    pool = Pool(hy, 1, B, H, D)
+    slots = list(rng.permutation(pool.alloc(B)))
+    S0 = (rng.standard_normal((B, H, D, D)) * 0.1).astype(np.float32)
+    for r, sl in enumerate(slots):
+        pool.view[0, sl] = torch.from_numpy(S0[r]).cuda()
+    dq, dk, dv = gu.dev(q), gu.dev(k), gu.dev(v)
+    do = torch.full_like(dq, float("nan"))
+    if gated:
+        hy.hyattn_linear_prefill_chunked_gated(pool.handle, 0, dq, dk, dv, gu.dev(g), do, gu.i32(cu),
+                                               gu.i32(slots), B, 64, hy.BF16)
+    else:
+        hy.hyattn_linear_prefill_chunked(pool.handle, 0, dq, dk, dv, do, gu.i32(cu), gu.i32(slots),
+                                         B, 64, hy.BF16)
+    torch.cuda.synchronize()
+    st = S0.astype(np.float64)
+    want = ref.linear_prefill(q, k, v, cu, st, chunk=64, log_gamma=g)
+    gu.assert_io(gu.host(do), want, "bf16", f"{B * H} units")
+    got_S = np.stack([gu.host(pool.view[0, sl]) for sl in slots])
+    gu.assert_f32(got_S, st, f"{B * H} units, states")
+    pool.close()
+
+
 def test_prefill_integer_inputs_bit_exact(hy):
     """bf16 MFMA path with small-integer inputs: exact results (all sums < 2^24)."""
     rng = np.random.default_rng(8)

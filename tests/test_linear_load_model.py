@@ -1,6 +1,7 @@
-"""CPU model of every memory access of the bf16 chunked-prefill kernel's block
-ring (k_linear_prefill_bf16 in linear_attention_attn_amd/csrc/k_linear.hip),
-checked against the buffers it may touch.
+"""CPU model of every memory access of the bf16 chunked-prefill kernels' block
+ring (k_linear_prefill_bf16 and k_linear_prefill_m32 in
+linear_attention_attn_amd/csrc/k_linear.hip, which issue the same loads),
+checked against the buffers they may touch.
 
 The kernel streams each (request, head)'s tokens in 32-token blocks through a
 3-slot LDS ring: per block, each of the 4 waves issues IPB global-to-LDS loads
@@ -171,3 +172,76 @@ def _model_one_head(tok0, T, H, D, N, gated, g, h):
             if gated:
                 t = np.minimum(BLOCK * b + (lanes & 31), T - 1)
                 assert ((tok0 + t) * H + h < N * H).all()
+
+
+def perm32(m):
+    g = m >> 3
+    return 16 * (g >> 1) + 8 * ((m >> 2) & 1) + 4 * (g & 1) + (m & 3)
+
+
+def test_perm32_is_a_permutation_with_the_stated_lane_layout():
+    """Row m of a 32-row operand stands for index perm32(m); the 32x32x16 product's
+    accumulator element i of a lane in half h holds row 8 (i / 4) + 4 h + i % 4, so
+    that lane must see index 16 (i / 8) + 8 h + i % 8."""
+    assert sorted(perm32(m) for m in range(32)) == list(range(32))
+    for h in range(2):
+        for i in range(16):
+            assert perm32(8 * (i // 4) + 4 * h + i % 4) == 16 * (i // 8) + 8 * h + i % 8
+
+
+def test_m32_fragment_and_state_accesses_stay_in_bounds():
+    """Every LDS read of the 32x32-tile kernel (Q and K fragments, transposing
+    reads of V and of K, the gated factors) stays inside its tile of the slot,
+    and every state and output element it touches lies in the head's D x D state
+    and in the block's rows (D = 128)."""
+    D, tile = 128, BLOCK * 128
+    lanes = np.arange(64)
+    lc, hl = lanes & 31, lanes >> 5
+    gi, gq = lanes & 15, (lanes >> 4) & 1
+    krow = np.array([perm32(int(m)) for m in lc])
+    for s in range(8):
+        col = 16 * s + 8 * hl
+        for rows, t in ((lc, 2), (krow, 0)):
+            x = np.array([swz(t, int(r), D) for r in rows])
+            e = rows * D + 8 * ((col >> 3) ^ x)
+            assert ((e >= 0) & (e + 8 <= tile)).all()
+    for w in range(4):
+        v0 = 32 * w
+        for tensor, bases in ((1, [v0]), (0, [32 * t for t in range(4)])):
+            for base in bases:
+                for c in range(2):
+                    row = 16 * c + 8 * hl + (gi >> 2)
+                    col = base + 16 * gq + 8 * (gi & 1) + 4 * ((gi >> 1) & 1)
+                    assert (col + 4 <= D).all() and (row + 4 < BLOCK).all()
+                    x = np.array([swz(tensor, int(r), D) for r in row])
+                    p = row * D + 8 * ((col >> 3) ^ x) + (col & 7)
+                    assert ((p >= 0) & (p + 4 + 4 * D <= tile)).all()
+                    # within each 16-lane group the transposing read hands lane i
+                    # element i % 4 of the chunk that source lane i / 4 (mod 4)
+                    # points at: column base + perm32(16 gq + i)
+                    for g in range(4):
+                        for i in range(16):
+                            got = int(col[16 * g + i // 4]) + i % 4
+                            assert got == base + perm32(16 * (g & 1) + i), (g, i, base)
+        # gated: each wave's 64 floats of forget factors after the three tiles
+        gsl = 2 * 3 * tile + 4 * (w * 64 + (lanes & 31))
+        assert ((gsl >= 2 * 3 * tile) & (gsl + 4 <= 2 * (3 * tile + 4 * 64 * 2))).all()
+        # state: rows 32 t + 16 (i >> 3) + 8 hl + (i & 7), column v0 + perm32(lc)
+        vcol = v0 + np.array([perm32(int(m)) for m in lc])
+        for t in range(4):
+            for i in range(16):
+                row = 32 * t + 16 * (i >> 3) + 8 * hl + (i & 7)
+                assert ((row >= 0) & (row < D) & (vcol >= 0) & (vcol < D)).all()
+        # output: row lc of the block (stored only when lc < n), 16-byte pieces at
+        # columns v0 + 8 hl + 16 a
+        for a in range(2):
+            c0 = v0 + 8 * hl + 16 * a
+            assert ((c0 >= 0) & (c0 + 8 <= D)).all()
+    # the state elements the four waves hold are each of the D x D elements once
+    seen = np.zeros((D, D), int)
+    for w in range(4):
+        vcol = 32 * w + np.array([perm32(int(m)) for m in lc])
+        for t in range(4):
+            for i in range(16):
+                seen[32 * t + 16 * (i >> 3) + 8 * hl + (i & 7), vcol] += 1
+    assert (seen == 1).all()
