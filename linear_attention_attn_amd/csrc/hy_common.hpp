@@ -70,6 +70,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Row m = 8 g + 4 h + j (g = 0..3, h = 0..1, j = 0..3) of a 32-row operand of
+// the product above taken to stand for index perm32(m) = 16 (g >> 1) + 8 h +
+// 4 (g & 1) + j of the 32 indices it covers: a lane of half h (lanes 32 h ..
+// 32 h + 31) then receives in accumulator element i the index
+// 16 (i >> 3) + 8 h + (i & 7), i.e. eight consecutive indices per half-tile,
+// which is a k operand of a following product (and a 16-byte bf16 piece).
+__device__ __forceinline__ int perm32(int m) {
+  const int g = m >> 3;
+  return 16 * (g >> 1) + 8 * ((m >> 2) & 1) + 4 * (g & 1) + (m & 3);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
 // i receives element i % 4 of the 8-byte chunks addressed by source lanes
 // 4 j + i / 4 (j = 0..3) of its group. Hence if source lane s points at

@@ -865,23 +865,13 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_bf16(
 //   P^T = K Q^T               the same 8 k steps (each Q fragment serves both)
 //   O^T += V^T tril(P)^T      2 k steps of 16 keys, P split hi + lo
 //   S  += K^T V               4 tiles x 2 k steps of 16 tokens
-// Rows of every 32-row operand are permuted by perm32 (see below), so that the
+// Rows of every 32-row operand are permuted by perm32 (hy_common.hpp), so that the
 // accumulator elements a lane holds are, per half-tile, eight consecutive
 // indices: exactly the k operand the next product needs, with no data
 // movement between lanes; the output then leaves as 16-byte pieces. The
 // contractions' operands otherwise come straight from the row-major tiles
 // (16-byte reads) or through transposing reads (K^T, V^T).
 // ============================================================================
-
-// Tile row m = 8 g + 4 h + j (g = 0..3, h = 0..1, j = 0..3) of a 32-row MFMA
-// operand stands for index perm32(m) = 16 (g >> 1) + 8 h + 4 (g & 1) + j of the
-// 32 key dims, keys or value columns it covers. A lane of half h (lanes 32 h ..
-// 32 h + 31) then receives in accumulator element i the index
-// 16 (i >> 3) + 8 h + (i & 7).
-__device__ __forceinline__ int perm32(int m) {
-  const int g = m >> 3;
-  return 16 * (g >> 1) + 8 * ((m >> 2) & 1) + 4 * (g & 1) + (m & 3);
-}
 
 template <bool GATED>
 __global__ __launch_bounds__(256, 2) void k_linear_prefill_m32(
@@ -952,18 +942,34 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_m32(
     }
   };
 
-  // ---- transposing reads: eight consecutive rows 16 c + 8 hl + 0..7 of one
-  // column of a tile, the column being base + perm32(lc). The lane's source
-  // address is row 16 c + 8 hl + gi / 4 (and 4 rows on), 4-column piece
-  // base + 16 gq + {0, 8, 4, 12}[gi % 4]: within each 16-lane group this hands
-  // lane gi the column perm32(16 gq + gi).
-  auto tr8 = [&](const uint16_t* tile, int c, int base, bool is_k) -> u32x4 {
-    const int row = 16 * c + 8 * hl + (gi >> 2);
-    const int col = base + 16 * gq + 8 * (gi & 1) + 4 * ((gi >> 1) & 1);
-    const uint16_t* p = tile + swz_off<D>(row, col, is_k ? kswz<D>(row) : vswz<D>(row));
-    const u32x2 a = ds_read_tr16_raw(p);
-    const u32x2 b2 = ds_read_tr16_raw(p + 4 * D);
-    return u32x4{a[0], a[1], b2[0], b2[1]};
+  // ---- transposing reads: for c = 0, 1 eight consecutive rows 16 c + 8 hl +
+  // 0..7 of one column of a tile, the column being base + perm32(lc). The
+  // lane's source address is row 16 c + 8 hl + gi / 4 (and 4 rows on, which
+  // share its chunk XOR), 4-column piece base + 16 gq + {0, 8, 4, 12}[gi % 4]:
+  // within each 16-lane group this hands lane gi the column
+  // perm32(16 gq + gi). All four reads go out as one opaque block led by an
+  // s_nop: an MFMA issued just before may still read registers the block
+  // overwrites (the previous tile's fragments), and the compiler, which pads
+  // its own LDS loads for that, does not see inside the block.
+  auto tr8x2 = [&](const uint16_t* tile, int base, bool is_k, u32x4 (&f)[2]) {
+    uint32_t a[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 16 * c + 8 * hl + (gi >> 2);
+      const int col = base + 16 * gq + 8 * (gi & 1) + 4 * ((gi >> 1) & 1);
+      const uint16_t* p = tile + swz_off<D>(row, col, is_k ? kswz<D>(row) : vswz<D>(row));
+      a[c] = static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)p));
+    }
+    u32x2 r0, r1, r2, r3;
+    asm volatile(
+        "s_nop 7\n"
+        "ds_read_b64_tr_b16 %0, %4\n ds_read_b64_tr_b16 %1, %4 offset:1024\n"
+        "ds_read_b64_tr_b16 %2, %5\n ds_read_b64_tr_b16 %3, %5 offset:1024"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a[0]), "v"(a[1]));
+    f[0] = u32x4{r0[0], r0[1], r1[0], r1[1]};
+    f[1] = u32x4{r2[0], r2[1], r3[0], r3[1]};
   };
 
   // state tiles: Sacc[t][i] = S[32 t + 16 (i >> 3) + 8 hl + (i & 7)][v0 + perm32(lc)]
@@ -1067,8 +1073,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_m32(
 
     // O^T += V^T P^T: V^T rows = value columns v0 + perm32(lc), keys 16 c + 8 hl + e
     u32x4 vt[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) vt[c] = tr8(Vt, c, v0, false);
+    tr8x2(Vt, v0, false, vt);
     lds_wait_all(vt);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -1109,8 +1114,7 @@ __global__ __launch_bounds__(256, 2) void k_linear_prefill_m32(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 kt[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) kt[c] = tr8(Kt, c, 32 * t, true);
+      tr8x2(Kt, 32 * t, true, kt);
       lds_wait_all(kt);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {

@@ -19,7 +19,8 @@ import pytest
 
 from linear_attention_attn_amd import _build
 
-WAIT_STATES = 8  # covers the 7 a 16x16x32 bf16 MFMA needs
+WAIT_STATES = 8  # covers the 7 a 16x16x32 bf16 MFMA needs (the compiler pads its own LDS
+# loads after a 32x32x16 that reads the overwritten register as A or B by fewer)
 
 
 def _regs(tok):
