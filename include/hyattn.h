@@ -288,7 +288,15 @@ size_t hyattn_hybrid_workspace_bytes(const hyattn_batch* batch);
  * Per linear layer: chunked prefill of the prefill requests, then decode of
  * the decode requests. Per full layer: append the new K/V of every request,
  * causal prefill attention for the prefill requests, decode attention for
- * the decode requests. All launches go to `stream` in layer order. */
+ * the decode requests. Launches go to `stream` in layer order, except that a
+ * full layer with both prefill and decode requests runs its decode attention
+ * on a second stream that the library keeps per device: forked from `stream`
+ * after the append, joined back into `stream` (which waits for it) before the
+ * next layer. Everything the step enqueues is thus complete once `stream`
+ * reaches the point after the call. The fork and join are events, so the
+ * step can be captured into a graph from `stream`; steps launched from
+ * several host threads onto one device share that second stream and take
+ * turns at each fork. */
 hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
                                  const hyattn_layer_io* layers, const hyattn_batch* batch,
                                  hyattn_state_pool* pool, void* stream);

@@ -57,6 +57,48 @@ bool checked_mode() {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// A second stream per device (default priority) and the two events that fork
+// work onto it from the caller's stream and join it back. The hybrid step
+// runs a full layer's decode attention there beside the layer's prefill
+// attention: they read disjoint requests of the pools, and a decode
+// workgroup fits a CU beside a prefill workgroup (the prefill's matrix work
+// and the decode's HBM streaming then overlap). Created on first use, kept
+// until the process ends. Callers hold `mu` from fork to join, so steps
+// launched from several host threads onto one device take turns at that
+// point.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+hipError_t side_stream(SideStream** out) {
+  static std::mutex mu;
+  static SideStream per_dev[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+      if (f) hipEventDestroy(f);
+      hipStreamDestroy(st);
+      return e;
+    }
+    ss.s = st;
+    ss.fork = f;
+    ss.join = j;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 hyattn_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(HYATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -768,7 +810,15 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
     fprintf(stderr, "[hyattn] step: %d layers (%d linear, %d full) plan %s; %d prefill + %d decode\n",
             n_layers, n_lin, n_full, plan.c_str(), b->n_prefill, b->n_decode);
   }
-  // 3. launches in layer order (arguments validated above)
+  // 3. launches in layer order (arguments validated above). A full layer with
+  //    both prefill and decode requests forks its decode attention onto the
+  //    side stream after the append and joins it back before the next layer.
+  const bool fork_full = n_full > 0 && b->n_prefill > 0 && b->max_prefill_len > 0 && b->n_decode > 0;
+  SideStream* side = nullptr;
+  if (fork_full) {
+    hipError_t e = side_stream(&side);
+    if (e != hipSuccess) return hip_status(e, "hybrid step side stream");
+  }
   const size_t esz = bf16 ? 2 : 4;
   const int n_prefill_tok = b->n_prefill > 0 ? b->n_prefill_tokens : 0;
   const size_t off = (size_t)n_prefill_tok * b->H * b->D * esz;  // first decode row
@@ -793,18 +843,37 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
       e = hy::launch_paged_append(L.k, L.v, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
                                   b->max_blocks_per_seq, b->context_lens, b->cu_q_lens, B,
                                   max_q_len, b->H_kv, b->D, bf16, s);
-      if (e == hipSuccess && b->n_prefill > 0 && b->max_prefill_len > 0)
-        e = hy::launch_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
-                                     b->max_blocks_per_seq, b->context_lens, b->cu_seqlens,
-                                     b->max_prefill_len, b->n_prefill, b->H, b->H_kv, b->D,
-                                     b->scale, bf16, s);
-      if (e == hipSuccess && b->n_decode > 0)
-        e = hy::launch_paged_decode((const char*)L.q + off, (char*)L.o + off, L.k_pool, L.v_pool,
-                                    b->n_blocks,
-                                    b->block_tables + (size_t)b->n_prefill * b->max_blocks_per_seq,
-                                    b->max_blocks_per_seq, b->context_lens + b->n_prefill,
-                                    b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
-                                    b->workspace, bf16, s);
+      auto decode = [&](hipStream_t ds) {
+        return hy::launch_paged_decode((const char*)L.q + off, (char*)L.o + off, L.k_pool,
+                                       L.v_pool, b->n_blocks,
+                                       b->block_tables + (size_t)b->n_prefill * b->max_blocks_per_seq,
+                                       b->max_blocks_per_seq, b->context_lens + b->n_prefill,
+                                       b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
+                                       b->workspace, bf16, ds);
+      };
+      auto prefill = [&]() {
+        return hy::launch_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
+                                        b->max_blocks_per_seq, b->context_lens, b->cu_seqlens,
+                                        b->max_prefill_len, b->n_prefill, b->H, b->H_kv, b->D,
+                                        b->scale, bf16, s);
+      };
+      if (e == hipSuccess && fork_full) {
+        // decode on the side stream (after the append), prefill here, then join
+        std::lock_guard<std::mutex> lk(side->mu);
+        if ((e = hipEventRecord(side->fork, s)) == hipSuccess &&
+            (e = hipStreamWaitEvent(side->s, side->fork, 0)) == hipSuccess) {
+          const hipError_t ed = decode(side->s);
+          const hipError_t ep = ed == hipSuccess ? prefill() : hipSuccess;
+          // joined whatever the launches returned, so that all side-stream
+          // work is ordered before anything the caller queues next
+          e = hipEventRecord(side->join, side->s);
+          if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+          if (e == hipSuccess) e = ed != hipSuccess ? ed : ep;
+        }
+      } else {
+        if (e == hipSuccess && b->n_prefill > 0 && b->max_prefill_len > 0) e = prefill();
+        if (e == hipSuccess && b->n_decode > 0) e = decode(s);
+      }
     }
     if (e != hipSuccess) return hip_status(e, "hybrid step launch");
   }

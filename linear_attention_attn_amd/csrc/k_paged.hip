@@ -194,11 +194,13 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 // Wave w of a workgroup takes blocks w, w + 4, ... of the partition.
 //
 // K and V blocks reach LDS through direct global-to-LDS loads (no registers
-// hold data in flight), each wave keeping its own ring of 4 block slots:
-// block j + 3 is requested while block j is used, so three blocks (24 KiB
-// at D = 128) per wave are in flight behind the computation and the waves
-// never synchronise inside an item. One workgroup fills a CU's LDS, which
-// is what bounds the bytes in flight.
+// hold data in flight), each wave keeping its own ring of 2 block slots:
+// block j + 1 is requested once block j has landed and is used while block j
+// is, and the waves never synchronise inside an item. A workgroup takes
+// 72 KiB of LDS at D = 128 (64 KiB of rings), so two fit a CU (as many bytes
+// in flight per CU as one workgroup with 4-slot rings, and as fast alone),
+// and one fits beside a causal-prefill workgroup (64 KiB): the hybrid step
+// runs a full layer's decode beside its prefill on a second stream.
 //   scores: v_mfma_f32_16x16x32_bf16 with A = the 16 K rows of the block
 //           (each lane's K fragment lands at its own LDS offset), B = the G
 //           query heads padded to 16 columns; lane l holds keys 4*(l/16)+i
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
 //           transposing reads of the row-major, chunk-swizzled V tile.
 // The waves are merged by log-sum-exp at the end of the item.
 // ============================================================================
-constexpr int kDecodeRing = 4;  // block slots per wave
+constexpr int kDecodeRing = 2;  // block slots per wave
 // Cache policy of the K/V block loads (sc0 | nt): every byte is read once per
 // call, so the loads stream past the caches (measured 3-8 % faster than the
 // default policy on the random block tables of the decode workload).
@@ -326,10 +328,9 @@ __global__ __launch_bounds__(256) void k_paged_decode_bf16(
     blk_ring[NB - 1] = table(NB - 1);
 
     for (int j = 0; j < nbw; ++j) {
-      const int ahead = nbw - 1 - j;  // blocks requested after this one: min(ahead, NB - 2)
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPB));
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(IPB));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // block j landed: with two slots no later block has been requested yet
+      static_assert(NB == 2, "the wait below assumes a 2-slot ring");
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       const int32_t blk = blk_ring[0];
       const int ntok = ntok_of(j, blk);
       const uint16_t* kslot = ring + (j % NB) * SLOT;
