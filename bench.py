@@ -819,6 +819,9 @@ def main():
             "paged_prefill_mfma_frac": round(wl.paged_prefill_flops() / (comp["paged_prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "step_ms_from_components": round(comp["state_zero"] + n_lin * (lp + ld) + n_full * (
                 comp["paged_append"] + comp["paged_prefill"] + pd), 3),
+            "note": "each operation launched alone inside a decomposed step; the step itself runs "
+                    "each full layer's decode beside its prefill on a second stream, so "
+                    "ms_per_step is below step_ms_from_components",
         }
         roof_ms = out["step_roofline"]["component_roof_ms"]
         out["step_roofline"]["component_frac"] = {
