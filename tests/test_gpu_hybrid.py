@@ -38,6 +38,48 @@ def test_hybrid_step_slot_assignment_does_not_matter():
         assert np.array_equal(x, y)
 
 
+def test_hybrid_step_replays_from_a_captured_graph():
+    """The step (prefill and decode requests, so each full layer forks its decode onto
+    the library's second stream and joins it back) captured into a graph and replayed
+    three times, with the states and pools restored by eager copies and a device
+    synchronisation before each replay: every replay gives the eager step's outputs,
+    states and pools bit for bit."""
+    import torch
+    case = hybrid.small_case(seed=7, n_layers=8)
+    assert case["n_prefill"] > 0 and case["n_decode"] > 0
+    g = hybrid_run.setup_gpu(case)
+    hy, types, layers = g["hy"], g["types"], g["layers"]
+    live = [g["buf"]] + [d[x] for t, d in zip(types, layers) if t == 1 for x in ("k_pool", "v_pool")]
+    saved = [x.clone() for x in live]
+
+    def restore():
+        for a, b in zip(live, saved):
+            a.copy_(b)
+        for d in layers:
+            d["o"].fill_(float("nan"))
+        torch.cuda.synchronize()
+
+    def snapshot():
+        return [d["o"].clone() for d in layers] + [x.clone() for x in live]
+
+    hy.hyattn_hybrid_step(types, len(types), layers, g["batch"], g["pool"])
+    torch.cuda.synchronize()
+    want = snapshot()
+    restore()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hy.hyattn_hybrid_step(types, len(types), layers, g["batch"], g["pool"])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}, tensor {i}"
+    hy.hyattn_state_pool_destroy(g["pool"])
+
+
 @pytest.mark.parametrize("fault", ["block id out of range", "slot never zeroed",
                                    "context beyond max_context", "q lengths inconsistent"])
 def test_hybrid_step_checked_mode_rejects_before_any_launch(monkeypatch, fault):
