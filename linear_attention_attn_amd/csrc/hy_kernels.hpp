@@ -51,11 +51,18 @@ size_t decode_launch_bytes(int B, int H_q, int H_kv, int D, int max_context);
 constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
 hipError_t decode_scratch(void** out);
 
+// plan_ready: the work-item layout of these (ctx, max_context, B, H_q, H_kv, D,
+// max_blocks) already sits in `workspace` (launch_decode_plan, or an earlier
+// decode of the same requests on the same stream order), so the call skips it.
 hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
                                int64_t n_blocks, const int32_t* bt, int max_blocks,
                                const int32_t* ctx, int max_context,
                                int B, int H_q, int H_kv, int D, float scale, void* workspace,
-                               bool bf16, hipStream_t s);
+                               bool bf16, hipStream_t s, bool plan_ready = false);
+// The work-item layout of a bf16 decode of these requests into `workspace`,
+// as launch_paged_decode lays it out first.
+hipError_t launch_decode_plan(const int32_t* ctx, int max_context, int B, int H_q, int H_kv, int D,
+                              int max_blocks, void* workspace, hipStream_t s);
 
 // VALU paged attention for fp32 I/O (decode with cu_q = NULL, or causal prefill).
 hipError_t launch_paged_simple_f32(const void* q, void* o, const void* k_pool, const void* v_pool,

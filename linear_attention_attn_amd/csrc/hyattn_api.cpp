@@ -820,6 +820,15 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
     if (e != hipSuccess) return hip_status(e, "hybrid step side stream");
   }
   const size_t esz = bf16 ? 2 : 4;
+  // every full layer's decode serves the same requests: their work-item layout
+  // is computed once, here, and each decode launch reuses it from the workspace
+  const bool plan_once = n_full > 0 && b->n_decode > 0 && bf16;
+  if (plan_once) {
+    hipError_t e = hy::launch_decode_plan(b->context_lens + b->n_prefill, b->max_context,
+                                          b->n_decode, b->H, b->H_kv, b->D,
+                                          b->max_blocks_per_seq, b->workspace, s);
+    if (e != hipSuccess) return hip_status(e, "hybrid step decode plan");
+  }
   const int n_prefill_tok = b->n_prefill > 0 ? b->n_prefill_tokens : 0;
   const size_t off = (size_t)n_prefill_tok * b->H * b->D * esz;  // first decode row
   const int max_q_len = b->n_prefill > 0 ? std::max(b->max_prefill_len, 1) : 1;
@@ -849,7 +858,7 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
                                        b->block_tables + (size_t)b->n_prefill * b->max_blocks_per_seq,
                                        b->max_blocks_per_seq, b->context_lens + b->n_prefill,
                                        b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
-                                       b->workspace, bf16, ds);
+                                       b->workspace, bf16, ds, plan_once);
       };
       auto prefill = [&]() {
         return hy::launch_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,

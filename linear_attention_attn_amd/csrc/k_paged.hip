@@ -579,11 +579,22 @@ hipError_t launch_paged_simple_f32(const void* q, void* o, const void* k_pool, c
                                   max_q_len, B, H_q, H_kv, sl2, s);
 }
 
+hipError_t launch_decode_plan(const int32_t* ctx, int max_context, int B, int H_q, int H_kv, int D,
+                              int max_blocks, void* workspace, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const DecodePlan plan = decode_plan(max_context, (int64_t)B * H_kv);
+  int32_t* cu_parts = reinterpret_cast<int32_t*>(
+      (char*)workspace + decode_partials_bytes(B, H_q, D, plan.max_parts));
+  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, s, ctx, B, max_blocks,
+                     plan.part_blocks, plan.max_parts, cu_parts);
+  return hipGetLastError();
+}
+
 hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const void* v_pool,
                                int64_t n_blocks, const int32_t* bt, int max_blocks,
                                const int32_t* ctx, int max_context,
                                int B, int H_q, int H_kv, int D, float scale, void* workspace,
-                               bool bf16, hipStream_t s) {
+                               bool bf16, hipStream_t s, bool plan_ready) {
   if (B <= 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (!bf16) {
@@ -598,10 +609,11 @@ hipError_t launch_paged_decode(const void* q, void* o, const void* k_pool, const
   float* ws = (float*)workspace;
   int32_t* cu_parts = reinterpret_cast<int32_t*>(
       (char*)workspace + decode_partials_bytes(B, H_q, D, plan.max_parts));
-  hipLaunchKernelGGL(k_decode_plan, dim3(1), dim3(1024), 0, s, ctx, B, max_blocks,
-                     plan.part_blocks, plan.max_parts, cu_parts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!plan_ready) {
+    e = launch_decode_plan(ctx, max_context, B, H_q, H_kv, D, max_blocks, workspace, s);
+    if (e != hipSuccess) return e;
+  }
   // enough workers to fill the chip a few times over; each walks items with stride gridDim.x
   const long bound = (long)B * plan.max_parts;
   unsigned workers = (unsigned)(bound < 2048 ? bound : 2048);
