@@ -234,19 +234,6 @@ def assert_bf16(g, r, what="", delta=None):
     return mx, mean
 
 
-def assert_bf16_pair(a, b, what=""):
-    """Two bf16 results of one exact quantity, each the rounding of a value within the
-    fp32 rule of it (1e-4 * max(|r|, RMS of the vector)), differ element by element by
-    at most one bf16 ulp plus twice that rule (taken around b)."""
-    a64, b64 = as_f64(np.asarray(a)), as_f64(np.asarray(b))
-    rms = np.sqrt(np.mean(b64 * b64, axis=-1, keepdims=True))
-    _, e = np.frexp(np.maximum(np.abs(a64), np.abs(b64)))
-    bound = np.ldexp(1.0, e - 8) + 2 * TOL_F32 * np.maximum(np.abs(b64), rms)
-    bad = np.abs(a64 - b64) > bound
-    assert not bad.any(), f"{what}: {int(bad.sum())} outputs differ by more than one ulp + 2e-4"
-    return float(np.mean(a64 != b64))
-
-
 def assert_io(g, r, dtype: str, what="", delta=None):
     return assert_f32(g, r, what) if dtype == "f32" else assert_bf16(g, r, what, delta)
 

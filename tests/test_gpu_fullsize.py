@@ -5,7 +5,8 @@ Workloads (seeded, synthetic; recipes in synth.WORKLOADS):
   * linear decode batch: B=64, H=32, D=128, 256 decode steps from prior states
     ~ N(0,1)*0.1, bf16 q/k/v;
   * linear chunked prefill: B=8, H=32, D=128, T=8192, chunk sizes 64/128/256,
-    from a zeroed state; outputs must agree across chunk sizes;
+    from a zeroed state; each chunk size against the oracle's sums at that size,
+    and the kernel's outputs the same bits at every chunk size;
   * paged decode: B=128, H_q=32, H_kv=8, D=128, contexts uniform in
     [512, 32768], 16-token blocks in a randomly permuted pool with 1024
     NaN-poisoned spare blocks;
@@ -116,12 +117,12 @@ def test_linear_prefill_8x8192_all_chunk_sizes(hy):
         outs[C] = oh
         hy.hyattn_state_pool_destroy(pool)
         del buf
-    # Chunk size only regroups the sums (P2 §2.4): each run's value before its
-    # final bf16 rounding meets the fp32 rule, so two chunk sizes differ by at
-    # most one bf16 ulp plus twice that rule, over the whole tensor.
+    # Chunk size only regroups the sums (P2 §2.4). The bf16 kernel streams the
+    # tokens in 32-token blocks whatever C is, so its outputs are the same bits
+    # at every C, while each C was checked above against the oracle's own
+    # C-chunked sums.
     for C in cfg["chunks"][1:]:
-        frac = gu.assert_bf16_pair(outs[C], outs[cfg["chunks"][0]], f"C={C} vs C={cfg['chunks'][0]}")
-        assert frac < 1e-2, f"C={C}: too many outputs differ"
+        assert np.array_equal(outs[C], outs[cfg["chunks"][0]]), f"C={C}: output depends on C"
 
 
 def test_paged_decode_b128_contexts_to_32k(hy):

@@ -224,7 +224,7 @@ def test_prefill_integer_inputs_bit_exact(hy):
 
 
 def test_chunk_size_invariance_and_continuation(hy):
-    """Outputs agree across chunk sizes; prefill(T) + decodes == prefill(T + n) (P2 §2.4, §4.1)."""
+    """Every chunk size against the oracle; prefill(T) + decodes == prefill(T + n) (P2 §2.4, §4.1)."""
     import torch
     rng = np.random.default_rng(9)
     H, D, T, extra = 2, 128, 200, 5
@@ -249,8 +249,10 @@ def test_chunk_size_invariance_and_continuation(hy):
         gu.assert_f32(gu.host(pool.view[0, 0])[None], st, f"C={chunk} state")
         outs[chunk] = got
         pool.close()
+    # the bf16 kernel streams 32-token blocks whatever the chunk size (each size
+    # was checked above against the oracle), so its outputs are the same bits
     for c in (16, 128):
-        gu.assert_bf16_pair(outs[c], outs[64], f"C={c} vs C=64")
+        assert np.array_equal(outs[c], outs[64]), f"C={c}: output depends on the chunk size"
 
 
 def test_batch_consistency_and_slot_isolation(hy):
