@@ -29,6 +29,9 @@ size_t linear_prefill_bf16_lds_bytes(int D, int C, bool gated);
 // Largest chunk the fp32-I/O prefill kernel takes (its chunk scores live in LDS).
 constexpr int kMaxChunkF32 = 128;
 
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* out);
+
 // ---- full layers --------------------------------------------------------------
 hipError_t launch_paged_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                int64_t n_blocks, const int32_t* bt, int max_blocks,
@@ -70,10 +73,13 @@ hipError_t launch_paged_simple_f32(const void* q, void* o, const void* k_pool, c
                                    const int32_t* ctx, const int32_t* cu_q, int max_q_len, int B,
                                    int H_q, int H_kv, int D, float scale, hipStream_t s);
 
+// grid_cap > 0 (bf16): at most that many workgroups, each walking several
+// query tiles (the hybrid step passes the CU count when the layer's decode runs
+// beside the prefill, so that every CU keeps room for decode workgroups).
 hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
                                 int64_t n_blocks, const int32_t* bt, int max_blocks,
                                 const int32_t* ctx,
                                 const int32_t* cu_q, int max_q_len, int B, int H_q, int H_kv,
-                                int D, float scale, bool bf16, hipStream_t s);
+                                int D, float scale, bool bf16, hipStream_t s, int grid_cap = 0);
 
 }  // namespace hy

@@ -815,8 +815,10 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
   //    side stream after the append and joins it back before the next layer.
   const bool fork_full = n_full > 0 && b->n_prefill > 0 && b->max_prefill_len > 0 && b->n_decode > 0;
   SideStream* side = nullptr;
+  int n_cus = 0;
   if (fork_full) {
     hipError_t e = side_stream(&side);
+    if (e == hipSuccess) e = hy::device_cus(&n_cus);
     if (e != hipSuccess) return hip_status(e, "hybrid step side stream");
   }
   const size_t esz = bf16 ? 2 : 4;
@@ -860,19 +862,21 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
                                        b->max_context, b->n_decode, b->H, b->H_kv, b->D, b->scale,
                                        b->workspace, bf16, ds, plan_once);
       };
-      auto prefill = [&]() {
+      auto prefill = [&](int grid_cap) {
         return hy::launch_paged_prefill(L.q, L.o, L.k_pool, L.v_pool, b->n_blocks, b->block_tables,
                                         b->max_blocks_per_seq, b->context_lens, b->cu_seqlens,
                                         b->max_prefill_len, b->n_prefill, b->H, b->H_kv, b->D,
-                                        b->scale, bf16, s);
+                                        b->scale, bf16, s, grid_cap);
       };
       if (e == hipSuccess && fork_full) {
         // decode on the side stream (after the append), prefill here, then join
         std::lock_guard<std::mutex> lk(side->mu);
         if ((e = hipEventRecord(side->fork, s)) == hipSuccess &&
             (e = hipStreamWaitEvent(side->s, side->fork, 0)) == hipSuccess) {
+          // beside the decode the prefill runs one persistent workgroup per CU,
+          // so that every CU keeps room for decode workgroups
           const hipError_t ed = decode(side->s);
-          const hipError_t ep = ed == hipSuccess ? prefill() : hipSuccess;
+          const hipError_t ep = ed == hipSuccess ? prefill(n_cus) : hipSuccess;
           // joined whatever the launches returned, so that all side-stream
           // work is ordered before anything the caller queues next
           e = hipEventRecord(side->join, side->s);
@@ -880,7 +884,7 @@ hyattn_status hyattn_hybrid_step(const int32_t* layer_types, int n_layers,
           if (e == hipSuccess) e = ed != hipSuccess ? ed : ep;
         }
       } else {
-        if (e == hipSuccess && b->n_prefill > 0 && b->max_prefill_len > 0) e = prefill();
+        if (e == hipSuccess && b->n_prefill > 0 && b->max_prefill_len > 0) e = prefill(0);
         if (e == hipSuccess && b->n_decode > 0) e = decode(s);
       }
     }

@@ -1164,8 +1164,7 @@ static hipError_t allow_lds(K kernel, size_t bytes) {
   return e;
 }
 
-// Compute units of the current device (cached per device).
-static hipError_t device_cus(int* out) {
+hipError_t device_cus(int* out) {
   static std::mutex mu;
   static std::map<int, int> cus;
   int dev = 0;

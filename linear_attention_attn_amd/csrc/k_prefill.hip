@@ -13,6 +13,8 @@
 // scale * log2(e), with a running reference subtracted (fp32 throughout).
 #include <math.h>
 
+#include <algorithm>
+
 #include "hy_common.hpp"
 #include "hy_kernels.hpp"
 
@@ -106,7 +108,7 @@ template <> __device__ __forceinline__ void tr_block<64>(const uint32_t (&a)[4],
   for (int i = 0; i < 4; ++i) vf[i] = u32x4{r[2 * i][0], r[2 * i][1], r[2 * i + 1][0], r[2 * i + 1][1]};
 }
 
-template <int D, int G, int NR>
+template <int D, int G, int NR, bool PERSIST>
 __global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t n_blocks, const int32_t* __restrict__ bt,
@@ -131,8 +133,10 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
   // pair together, heaviest (longest causal span) first: the tiles in flight
   // on an XCD stream the same pair's keys, which its L2 then holds, and the
   // shortest tiles fill the tail. Ids past the last pair exit at once.
+  // PERSIST: the same ids, walked by a smaller grid (see the end).
   const int n_gr = H_kv * n_req;
-  const int xcd = (int)blockIdx.x & 7, jx = (int)blockIdx.x >> 3;
+  auto item = [&](const int id) {
+  const int xcd = id & 7, jx = id >> 3;
   const int pslot = jx / n_qt;
   const int pair = pslot * 8 + xcd;
   if (pair >= n_gr) return;
@@ -373,6 +377,9 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
   int32_t blk_ring[NB];  // block ids of the stages in flight (wave-uniform)
   // the Q fragments land first, so no later wait for them can drain the ring
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // a workgroup that walks several items: every wave is done with the previous
+  // item's stage buffers before any wave requests this item's first stages
+  if constexpr (PERSIST) __syncthreads();
 #pragma unroll
   for (int i = 0; i < NB - 1; ++i) {
     blk_ring[i] = block_of(i);
@@ -425,25 +432,45 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
       *reinterpret_cast<u32x2*>(op + 16 * dt) = t;
     }
   }
+  };
+  if constexpr (PERSIST) {
+    // persistent: a grid of at most one workgroup per CU walks the ids with
+    // stride gridDim.x (a multiple of 8, so each workgroup stays on its XCD's
+    // ids, in the order above)
+    const int n_ids = n_qt * 8 * ((n_gr + 7) / 8);
+    for (int id = (int)blockIdx.x; id < n_ids; id += (int)gridDim.x) item(id);
+  } else {
+    item((int)blockIdx.x);
+  }
 }
 
 hipError_t launch_paged_prefill(const void* q, void* o, const void* k_pool, const void* v_pool,
                                 int64_t n_blocks, const int32_t* bt, int max_blocks,
                                 const int32_t* ctx,
                                 const int32_t* cu_q, int max_q_len, int B, int H_q, int H_kv,
-                                int D, float scale, bool bf16, hipStream_t s) {
+                                int D, float scale, bool bf16, hipStream_t s, int grid_cap) {
   if (B <= 0 || max_q_len <= 0) return hipSuccess;
   const float sl2 = scale * kLog2e;
   if (bf16) {
     const int G = H_q / H_kv;
+    // grid_cap > 0: at most that many workgroups (rounded down to a multiple of
+    // 8), each walking several ids (the persistent form)
+    const int cap = grid_cap > 0 ? std::max(8, grid_cap & ~7) : 0;
 #define HY_PP(DD, GG)                                                                          \
   do {                                                                                         \
     constexpr int QT_ = 64 * kPrefillNR / GG;                                                  \
     const int n_qt = (max_q_len + QT_ - 1) / QT_;                                              \
-    dim3 grid((unsigned)(n_qt * 8 * ((H_kv * B + 7) / 8)));                                    \
-    hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR>), grid, dim3(256), 0, s, (const uint16_t*)q, \
-                       (uint16_t*)o, (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, \
-                       bt, max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                    \
+    const int n_ids = n_qt * 8 * ((H_kv * B + 7) / 8);                                         \
+    if (cap > 0 && cap < n_ids)                                                                \
+      hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR, true>), dim3((unsigned)cap), \
+                         dim3(256), 0, s, (const uint16_t*)q, (uint16_t*)o,                    \
+                         (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, bt,       \
+                         max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                      \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_paged_prefill_bf16<DD, GG, kPrefillNR, false>), dim3((unsigned)n_ids), \
+                         dim3(256), 0, s, (const uint16_t*)q, (uint16_t*)o,                    \
+                         (const uint16_t*)k_pool, (const uint16_t*)v_pool, n_blocks, bt,       \
+                         max_blocks, ctx, cu_q, H_q, H_kv, sl2, n_qt, B);                      \
   } while (0)
 #define HY_PP_G(DD)                   \
   switch (G) {                        \

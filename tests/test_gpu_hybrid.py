@@ -29,6 +29,25 @@ def test_hybrid_step_matches_oracle(kw):
     hybrid_run.compare(case, got, want)
 
 
+def test_hybrid_step_prefill_beside_decode_walks_several_tiles_per_workgroup():
+    """A full layer whose prefill has more query-tile work items than the device has
+    CUs, with decode requests beside it: the step then runs the prefill as one
+    persistent workgroup per CU (each walking several tiles) next to the decode on
+    the second stream. Outputs, states and pools against the oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H, Hkv = 4, 2
+    qt = 64 * 3 // (H // Hkv)           # query positions per work item
+    n_len = (cus // 8 + 2) * qt         # query tiles x 8 XCD slots > CUs
+    case = hybrid.small_case(seed=21, n_layers=4, H=H, Hkv=Hkv, prefill_lens=(n_len, 50),
+                             decode_ctx=(7, 700, 33), chunk=64)
+    n_qt = -(-n_len // qt)
+    assert n_qt * 8 * -(-(Hkv * 5) // 8) > cus
+    got = hybrid_run.run_gpu(case)
+    want = hybrid_run.run_oracle(case)
+    hybrid_run.compare(case, got, want)
+
+
 def test_hybrid_step_slot_assignment_does_not_matter():
     case = hybrid.small_case(seed=5)
     B = case["n_prefill"] + case["n_decode"]
