@@ -512,7 +512,10 @@ def kernel_workloads(emit=None):
             "attainable_roof_frac": round(t_roof / (t * 1e-3), 4)}
     done("linear_prefill", {"shape": f"{B}x{T} tokens H={H} D={D} bf16 io", "bytes": pf_bytes,
                             "flops_kernel_count": N * H * (4 * D * D + 2 * 33 * D),
-                            "chunks": per_c})
+                            "chunks": per_c,
+                            "note": "the bf16 kernel streams 32-token blocks whatever the chunk "
+                                    "size, so the chunk sizes time one kernel (the same output "
+                                    "bits); they differ only in the flop count of the chunk form"})
     hy.hyattn_state_pool_destroy(pool)
     del buf, q, k, v, o
 
