@@ -325,6 +325,9 @@ __global__ __launch_bounds__(256, 2) void k_paged_prefill_bf16(
     // its softmax ahead of the other wave's MFMAs, which then fill the matrix
     // pipe behind it: 5 % faster than equal priorities.
     __builtin_amdgcn_s_setprio(1);
+    // LLVM's interleaving of LDS reads with MFMAs for small products
+    // (iglp_opt 0) over the score phase: 4.5 % faster than its own schedule
+    __builtin_amdgcn_iglp_opt(0);
     scores(Kb, sc);
     if constexpr (decltype(diag)::value) mask(st * KT, sc);
     __builtin_amdgcn_s_setprio(2);
