@@ -16,8 +16,9 @@ Printed: one JSON line (see the keys below), with
   * the first (cold) step beside the steady state (first_step_ms),
   * each layer operation on a workload of its own (workloads: the 64-request
     linear decode batch cold and back to back, the 8 x 8192-token chunked
-    prefill per chunk size with its first call, the B = 128 paged decode;
-    see kernel_workloads()), timed before the step's workload is allocated,
+    prefill per chunk size with its first call, the B = 128 paged decode, the
+    step's 16 x 4096 causal prefill alone; see kernel_workloads()), timed before
+    the step's workload is allocated,
   * per-operation times on the step's own data (components_ms_per_call),
   * the fp64 oracle's throughput on a bounded sample of the same workload.
 
@@ -401,10 +402,13 @@ def kernel_workloads(emit=None):
         call, then the median of 10 after 3 warm-ups;
       * paged decode: B = 128, H_q = 32, H_kv = 8, D = 128, contexts uniform in
         [512, 32768], 16-token blocks in a permuted pool with 1024 NaN spare blocks:
-        the first call, then the median of 20 after 5 warm-ups.
+        the first call, then the median of 20 after 5 warm-ups;
+      * causal prefill: the hybrid step's full-layer prefill (16 requests x 4096 new
+        tokens, H_q = 32, H_kv = 8, D = 128) through hyattn_paged_prefill alone: the
+        first call, then the median of 10 after 3 warm-ups.
     A GPU-side sleep ahead of each timed call lets the host enqueue the events and the
     launch before the GPU reaches them, so host launch latency is not timed. Returns a
-    dict of the three workloads' figures (emit: called with each one as it is done).
+    dict of the four workloads' figures (emit: called with each one as it is done).
     Every device buffer is released before returning."""
     import torch
     from linear_attention_attn_amd import hyattn as hy
@@ -552,6 +556,37 @@ def kernel_workloads(emit=None):
         "gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
         "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     del kp, vp, q, o, ws, bt, ctx_d, spare
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ---- causal prefill: the hybrid step's full-layer prefill on its own ----
+    P, B = W["prefill_len"], W["n_prefill"]
+    Hq, Hkv, D = W["H"], W["Hkv"], W["D"]
+    rng = np.random.default_rng(W["seed"] + 100)
+    ctx = np.full(B, P, np.int32)
+    lay = synth.paged_layout(rng, ctx)
+    kp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, W["seed"] * 1000 + 11)
+    vp = synth.device_normal_bf16((lay.n_blocks, Hkv, 16, D), 1.0, W["seed"] * 1000 + 12)
+    q = synth.device_normal_bf16((B * P, Hq, D), 1.0, W["seed"] * 1000 + 13)
+    o = torch.empty_like(q)
+    bt = torch.as_tensor(lay.block_tables).to(dev)
+    ctx_d = torch.as_tensor(ctx).to(dev)
+    cu = torch.as_tensor(synth.cu_lens([P] * B)).to(dev)
+    call = lambda: hy.hyattn_paged_prefill(q, o, kp, vp, lay.n_blocks, bt, lay.max_blocks, ctx_d,
+                                           cu, P, B, Hq, Hkv, D, D ** -0.5, hy.BF16)
+    first = timed(call)
+    for _ in range(3):
+        timed(call)
+    t = float(np.median([timed(call) for _ in range(10)]))
+    flops = B * Hq * 4 * D * (P * (P + 1) // 2)
+    done("paged_prefill", {
+        "shape": f"{B} requests x {P} new tokens (empty context), causal, H_q={Hq} H_kv={Hkv} "
+                 f"D={D} bf16, 16-token blocks",
+        "first_call_ms": round(first, 4), "ms_median": round(t, 4),
+        "tokens_per_s": round(B * P / (t * 1e-3), 1), "flops": flops,
+        "tflops": round(flops / (t * 1e-3) / 1e12, 1),
+        "mfma_frac": round(flops / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)})
+    del kp, vp, q, o, bt, ctx_d, cu
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
