@@ -29,17 +29,17 @@ def test_hybrid_step_matches_oracle(kw):
     hybrid_run.compare(case, got, want)
 
 
-def test_hybrid_step_prefill_beside_decode_walks_several_tiles_per_workgroup():
+@pytest.mark.parametrize("H,Hkv,D", [(4, 2, 128), (8, 2, 64)])
+def test_hybrid_step_prefill_beside_decode_walks_several_tiles_per_workgroup(H, Hkv, D):
     """A full layer whose prefill has more query-tile work items than the device has
     CUs, with decode requests beside it: the step then runs the prefill as one
     persistent workgroup per CU (each walking several tiles) next to the decode on
     the second stream. Outputs, states and pools against the oracle."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    H, Hkv = 4, 2
     qt = 64 * 3 // (H // Hkv)           # query positions per work item
     n_len = (cus // 8 + 2) * qt         # query tiles x 8 XCD slots > CUs
-    case = hybrid.small_case(seed=21, n_layers=4, H=H, Hkv=Hkv, prefill_lens=(n_len, 50),
+    case = hybrid.small_case(seed=21 + D, n_layers=4, H=H, Hkv=Hkv, D=D, prefill_lens=(n_len, 50),
                              decode_ctx=(7, 700, 33), chunk=64)
     n_qt = -(-n_len // qt)
     assert n_qt * 8 * -(-(Hkv * 5) // 8) > cus
