@@ -53,6 +53,11 @@ constexpr int kPrefillNR = 3;
 //                  from registers)
 // Computing O^T rather than O keeps the softmax row, the score column and the
 // output column on the same lane, so rescaling needs no data movement.
+//
+// PERSIST = true: the same work items walked by a grid of at most one
+// workgroup per CU (the hybrid step's form beside a decode on a second
+// stream, which then keeps room on every CU), with a workgroup barrier before
+// each item's first stage requests.
 // ============================================================================
 template <int D>
 __host__ __device__ __forceinline__ int pf_kswz(int row) {  // chunk XOR of a K row of a stage
